@@ -1,0 +1,182 @@
+/*
+ * dspark.h — C ABI of libdspark: the DSpark Markov-head draft, the
+ * hardware-aware prefix scheduler and the prefix-match verify step, as
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles and sections only):
+ *   [P-blog] "DSpark: DeepSeek's new speculative decoding work (Video + Blog)"
+ *   [P-wisp] "DSpark: Overcoming the Efficiency Wall in LLM Speculative Decoding"
+ *   [P-news] "DeepSeek's DSpark just fixed the two things that held back
+ *             faster AI inference"
+ *
+ * Conventions for every entry point
+ *   - Array arguments are DEVICE pointers to contiguous row-major storage
+ *     owned by the caller.  The library keeps no pointer once the enqueued
+ *     work has finished and allocates no device memory on these calls; all
+ *     scratch memory comes from the caller's `workspace`.
+ *   - Work is enqueued on `stream` and the call returns; outputs are valid
+ *     once the stream has been synchronised.
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     an error nothing is launched and outputs are left untouched.  Errors
+ *     are reported by the return code; dspark_last_error() gives a
+ *     thread-local message for the last failing call of the calling thread.
+ *   - Nothing aborts or prints.
+ *   - Token ids outside [0, V) are clamped to the vocabulary before any
+ *     memory access (results are then meaningless but memory stays in
+ *     bounds).  Inputs must be finite.
+ *   - Calls are reentrant; concurrent calls need separate workspaces.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int dspark_status;
+enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad enum      */
+  DSPARK_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle  */
+  DSPARK_ERR_WORKSPACE = 3,    /* workspace missing, too small or misaligned */
+  DSPARK_ERR_HIP = 4           /* a HIP runtime call or launch failed        */
+};
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;     /* storage of U, h, W1, W2 */
+typedef enum { DSPARK_GREEDY = 0, DSPARK_GUMBEL = 1 } dspark_sampling;
+
+/* Bytes of workspace dspark_markov_draft needs for this shape (a multiple of
+ * 256).  Returns 0 for B*gamma == 0.  Needs no GPU. */
+size_t dspark_draft_workspace_bytes(int B, int gamma, int V, int r);
+
+/*
+ * dspark_markov_draft — one block of semi-autoregressive drafting with the
+ * Markov sequential head, its confidence head, Sequential Temperature
+ * Scaling and the prefix-survival product.
+ *
+ * Defined by: [P-blog] §4 "Semi-Autoregressive Generation" (parallel stage:
+ * the anchor is the first prediction position, so gamma positions give gamma
+ * base logit vectors U_k; sequential stage: transition bias added to U_k;
+ * Markov head: first-order transition B(x_{k-1}, x_k), low-rank B = W1 W2
+ * with W1 an embedding lookup and W2 a logits projection); [P-blog] §5
+ * "Confidence-Scheduled Verification" (c_k from a linear projection and a
+ * sigmoid of the backbone hidden state at k and the Markov embedding of the
+ * previous draft token; Sequential Temperature Scaling with one temperature
+ * per position; the cumulative product as the prefix survival); [P-news]
+ * "How DSpark combines the best of both worlds" (rank-256 factorisation).
+ *
+ * For every request b and k = 1..gamma, with x_0 = anchor[b]:
+ *   e       = W1[x_{k-1}]                                    (gather)
+ *   z_k(v)  = U[b][k-1][v] + sum_j e[j] * W2[j][v]           (fp32 accumulate)
+ *   x_k     = smallest v maximising z_k(v)            (GREEDY)
+ *           = smallest v maximising z_k(v) + G(seed,b,k,v)   (GUMBEL)
+ *   c_k     = 1 / (1 + exp(-(conf_w . [h[b][k-1] ; e] + conf_b) / sts_T[k-1]))
+ *   S_k     = S_{k-1} * c_k   (S_0 = 1, fp32 multiply)
+ * G is standard Gumbel noise -ln(-ln u) from the Philox4x32-10 counter-based
+ * generator: key = (seed low 32 bits, seed high 32 bits), counter =
+ * (v >> 2, k, b, 0), output word v & 3, u = (2 * (word >> 9) + 1) * 2^-24.
+ *
+ * Arguments
+ *   B, gamma      requests, draft positions per request (0 is a no-op)
+ *   V, r, d       vocabulary size, Markov rank, backbone hidden size
+ *   dtype         storage of U, h, W1, W2: DSPARK_F32 (r % 4 == 0, r <= 64)
+ *                 or DSPARK_BF16 (r % 32 == 0, r <= 256)
+ *   anchor  int32 [B]                x_0 per request
+ *   U             [B][gamma][V]      base logits U_k
+ *   h             [B][gamma][d]      backbone hidden states h_k
+ *   W1            [V][r]             transition embedding table
+ *   W2            [r][V]             transition logits projection
+ *   conf_w  fp32  [d + r]            hidden-state weights first, then embedding weights
+ *   conf_b        confidence bias
+ *   sts_T   fp32  [gamma]            T_1..T_gamma (> 0)
+ *   mode, seed    sampling rule; seed used only for DSPARK_GUMBEL
+ *   tokens  int32 [B][gamma] out     x_1..x_gamma
+ *   logit   fp32  [B][gamma] out     z_k(x_k), without Gumbel noise
+ *   conf    fp32  [B][gamma] out     c_k
+ *   surv    fp32  [B][gamma] out     S_k
+ *   workspace     >= dspark_draft_workspace_bytes(B, gamma, V, r) bytes,
+ *                 256-byte aligned; contents on entry are ignored
+ * Limits: gamma <= 64, d <= 65536, V <= 2^24 and V small enough that the
+ * GPU's compute units can hold W2 on chip (V <= 163840 on MI355X);
+ * otherwise DSPARK_ERR_UNSUPPORTED.
+ */
+dspark_status dspark_markov_draft(
+    int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+    const int32_t* anchor, const void* U, const void* h, const void* W1, const void* W2,
+    const float* conf_w, float conf_b, const float* sts_T,
+    dspark_sampling mode, uint64_t seed,
+    int32_t* tokens, float* logit, float* conf, float* surv,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_schedule — hardware-aware prefix scheduler: per-request verify
+ * lengths that maximise expected committed tokens per unit of verify-step
+ * cost.
+ *
+ * Defined by: [P-wisp] "2. The Hardware-Aware Prefix Scheduler" (throughput
+ * maximisation from calibrated survival probabilities and the current
+ * steps-per-second curve; per-request verify lengths); [P-blog] §6 (global
+ * throughput maximisation; verify cost depends on load); [P-blog] §3 (the
+ * low-confidence suffix is dropped); [P-news] "Confidence-scheduled
+ * verification" (strict prefix-matching survival).
+ *
+ * With n = B + M verify tokens (each request's anchor plus M drafts), choose
+ * lens in {0..gamma}^B with sum lens = M maximising
+ *   Phi = (B + sum_i sum_{k <= lens_i} S_{i,k}) / t_step[n - n_min].
+ * Exactly: all (i, k) are ranked by (S desc, i asc, k asc); gains are the
+ * fixed-point values rint(S * 2^32) (ties to even) summed in int64; Phi(M)
+ * is one IEEE fp64 division of (B * 2^32 + sum of the top-M gains) by
+ * t_step[B + M - n_min]; M* is the smallest M with the largest Phi over
+ * M = 0..min(B*gamma, n_min + n_count - 1 - B); lens_i counts request i's
+ * entries among the top M*.
+ *
+ * Arguments
+ *   surv   fp32 [B][gamma]   prefix survivals, each row non-increasing, in [0, 1]
+ *   t_step fp64 [n_count]    verify-step cost for n = n_min .. n_min + n_count - 1 (> 0)
+ *   n_min, n_count           need n_min <= B <= n_min + n_count - 1
+ *   lens      int32 [B] out
+ *   m_out     int32 [1] out  M*
+ *   objective fp64  [1] out  Phi(M*) / 2^32 (may be NULL)
+ * Limits: B * gamma <= 16384 (one workgroup sorts in LDS), else
+ * DSPARK_ERR_UNSUPPORTED.
+ */
+dspark_status dspark_schedule(
+    int B, int gamma, const float* surv, const double* t_step, int n_min, int n_count,
+    int32_t* lens, int32_t* m_out, double* objective, hipStream_t stream);
+
+/*
+ * dspark_verify — strict prefix-match verification of the scheduled drafts.
+ *
+ * Defined by: [P-news] opening (the target verifies the block in one pass;
+ * accepted tokens stick, the first rejected token and everything after it
+ * are dropped); [P-blog] §3 (the target verifies the scheduled prefix; the
+ * next anchor is the target's bonus token).
+ *
+ *   accepted[b] = largest a <= lens[b] with tokens[b][j] == target[b][j] for all j < a
+ *   bonus[b]    = target[b][accepted[b]]
+ *
+ * Arguments
+ *   tokens int32 [B][gamma]      drafts x_1..x_gamma
+ *   target int32 [B][gamma + 1]  the target model's tokens at positions 1..gamma+1
+ *   lens   int32 [B]             scheduled lengths (clamped to [0, gamma])
+ *   accepted, bonus int32 [B] out
+ */
+dspark_status dspark_verify(
+    int B, int gamma, const int32_t* tokens, const int32_t* target, const int32_t* lens,
+    int32_t* accepted, int32_t* bonus, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* dspark_status_string(dspark_status s);
+
+/* Message for the calling thread's last failing call ("" if none). */
+const char* dspark_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

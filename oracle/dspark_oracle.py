@@ -1,0 +1,278 @@
+"""CPU oracle for the DSpark Markov-head draft, prefix scheduler and verify step.
+
+TEST INFRASTRUCTURE.  Only the tests, the package entry's smoke check and the
+benchmark's CPU-baseline leg may import this module.  The library never does:
+it shares no code, table or helper with the HIP path.
+
+Plain, slow and written to be checked against the pages by eye: numpy in fp64,
+one vocabulary-wide matrix product per draft step (a library primitive), no
+blocking or fusion.  Where a floating-point value decides an integer (the
+argmax that picks a draft token) the decision is taken on the value rounded to
+fp32, the precision the GPU kernel decides in.
+
+Pages cited (titles and sections only):
+  [P-blog]  "DSpark: DeepSeek's new speculative decoding work (Video + Blog)"
+  [P-wisp]  "DSpark: Overcoming the Efficiency Wall in LLM Speculative Decoding"
+  [P-news]  "DeepSeek's DSpark just fixed the two things that held back faster
+             AI inference"
+
+Readings taken where the pages are silent or garbled are listed in the
+repository's design notes; the ones that matter for a function are restated in
+its docstring.  Every function here is pinned by a "not gpu" test against
+something other than itself (explicit V x V matrix, textbook routines, brute
+force, closed forms, published Philox known-answer vectors, statistics).
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Optional
+
+import numpy as np
+
+TWO32 = float(2 ** 32)
+
+
+# ----------------------------------------------------------------------------
+# storage decoding
+# ----------------------------------------------------------------------------
+def widen(a: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of a stored tensor: uint16 arrays hold bfloat16 bit
+    patterns (sign, 8-bit exponent, 7-bit mantissa: the top half of an fp32),
+    float32 arrays are widened as is."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported storage dtype {a.dtype}")
+
+
+# ----------------------------------------------------------------------------
+# Philox4x32-10 and Gumbel noise (stochastic drafting)
+# ----------------------------------------------------------------------------
+_PHILOX_M0 = 0xD2511F53
+_PHILOX_M1 = 0xCD9E8D57
+_PHILOX_W0 = 0x9E3779B9
+_PHILOX_W1 = 0xBB67AE85
+_MASK32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+    numbers: as easy as 1, 2, 3", SC'11, section on the Philox family).
+
+    One round maps the counter (c0, c1, c2, c3) under key (k0, k1) to
+    (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0)) where
+    hi/lo are the upper/lower 32 bits of the 64-bit product; between rounds
+    the key is advanced by the Weyl constants (W0, W1).  Arrays broadcast.
+    Returns four uint32 arrays."""
+    c0, c1, c2, c3 = (np.asarray(x, dtype=np.uint64) & _MASK32 for x in (c0, c1, c2, c3))
+    k0 = np.uint64(int(k0) & 0xFFFFFFFF)
+    k1 = np.uint64(int(k1) & 0xFFFFFFFF)
+    m0, m1 = np.uint64(_PHILOX_M0), np.uint64(_PHILOX_M1)
+    for rnd in range(10):
+        if rnd:
+            k0 = np.uint64((int(k0) + _PHILOX_W0) & 0xFFFFFFFF)
+            k1 = np.uint64((int(k1) + _PHILOX_W1) & 0xFFFFFFFF)
+        p0 = m0 * c0
+        p1 = m1 * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & _MASK32,
+                          (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & _MASK32)
+    return tuple(x.astype(np.uint32) for x in (c0, c1, c2, c3))
+
+
+def gumbel_uniform_bits(seed: int, b, k: int, v):
+    """Raw 32-bit hash word for (seed, request b (0-based), position k
+    (1-based), vocabulary id v (0-based)).
+
+    Reading: counter = (v >> 2, k, b, 0), key = (low, high 32 bits of seed),
+    and the word used is output word (v & 3), so one Philox evaluation serves
+    four neighbouring vocabulary ids."""
+    v = np.asarray(v, dtype=np.int64)
+    b = np.asarray(b, dtype=np.int64)
+    words = philox4x32_10(v >> 2, np.full_like(v, k), b, np.zeros_like(v),
+                          seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    sel = (v & 3).astype(np.int64)
+    w = np.choose(sel, words)
+    return w.astype(np.uint32)
+
+
+def gumbel_noise(seed: int, b, k: int, v) -> np.ndarray:
+    """G = -ln(-ln u) with u = (2*(word >> 9) + 1) * 2^-24, an odd multiple of
+    2^-24 in (0, 1) (exact in fp32).  Evaluated in fp64, rounded to fp32."""
+    w = gumbel_uniform_bits(seed, b, k, v).astype(np.float64)
+    u = (np.floor(w / 512.0) * 2.0 + 1.0) * 2.0 ** -24
+    return (-np.log(-np.log(u))).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Draft: Markov head + confidence head + STS + prefix survival
+# ----------------------------------------------------------------------------
+def sigmoid64(x: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def draft(anchor, U, h, W1, W2, conf_w, conf_b, sts_T, sampling: str = "greedy",
+          seed: int = 0, rows=None, choose: Optional[Callable] = None,
+          trace: Optional[list] = None):
+    """Semi-autoregressive drafting with the Markov head.
+
+    For each request b (rows of the batch; every request's chain is
+    independent) and each draft position k = 1..gamma:
+
+    1. Gather e = W1[x_{k-1}], the Markov embedding of the previous draft
+       token, with x_0 the anchor ([P-blog] §4, "Two instantiations of the
+       sequential block", Markov head: W1 is an embedding lookup table; the
+       anchor is the first prediction position, §4 parallel stage).
+    2. Transition bias row B(x_{k-1}, .) = e @ W2, the low-rank factorisation
+       B = W1 W2 of the first-order V x V transition ([P-blog] §4 Markov head;
+       [P-news] "How DSpark combines the best of both worlds").
+    3. Logits z_k = U_k + bias, U_k the backbone's base logits at position k
+       ([P-blog] §4 sequential stage).  Computed in fp64, rounded to fp32.
+    4. Draft token x_k = the lowest vocabulary id with the largest score, the
+       score being z_k (greedy) or z_k + G(seed, b, k, v) in fp32 (Gumbel-max
+       sampling from softmax(z_k)).  Reading: the pages lose the formula of
+       the drafting distribution; p_k(v) is taken proportional to exp(z_k(v)).
+    5. Confidence c_k = sigmoid((w . [h_k ; e] + b) / T_k): a linear
+       projection of the backbone hidden state at k and the Markov embedding
+       of the previous draft token, then a sigmoid ([P-blog] §5), with the
+       sequential temperature T_k dividing the whole pre-sigmoid value
+       ([P-blog] §5 "Sequential Temperature Scaling"; [P-wisp] "Critical
+       Insights").  The dot product is accumulated in fp64; c_k is rounded to
+       fp32.
+    6. Prefix survival S_k = S_{k-1} * c_k with S_0 = 1, one fp32 multiply
+       ([P-blog] §5 "cumulative product"; [P-news] "strict prefix-matching
+       survival process").
+
+    `choose(k, rows, s, x)` may replace the oracle's token choice at step k
+    (s: fp32 scores [n, V], x: the oracle's argmax); the chain continues from
+    whatever it returns.  `trace`, if a list, receives per-step dicts with the
+    fp64 logits and the gathered embeddings.
+
+    Returns (tokens int32 [n, gamma], zsel fp32 [n, gamma], conf fp32,
+    surv fp32), zsel being the unperturbed logit z_k(x_k).
+    """
+    U = np.asarray(U)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    d = h.shape[2]
+    rows = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = rows.size
+    W2f = widen(W2)
+    wf = np.asarray(conf_w, dtype=np.float32).astype(np.float64)
+    w_h, w_e = wf[:d], wf[d:d + r]
+    T = np.asarray(sts_T, dtype=np.float32).astype(np.float64)
+    tokens = np.zeros((n, gamma), dtype=np.int32)
+    zsel = np.zeros((n, gamma), dtype=np.float32)
+    conf = np.zeros((n, gamma), dtype=np.float32)
+    surv = np.zeros((n, gamma), dtype=np.float32)
+    x_prev = np.asarray(anchor, dtype=np.int64)[rows]
+    S = np.ones(n, dtype=np.float32)
+    vv = np.arange(V, dtype=np.int64)
+    ar = np.arange(n)
+    for k in range(1, gamma + 1):
+        e = widen(W1[x_prev])                                   # step 1
+        z64 = widen(U[rows, k - 1]) + e @ W2f                   # steps 2-3
+        z = z64.astype(np.float32)
+        if sampling == "greedy":
+            s = z
+        elif sampling == "gumbel":
+            G = gumbel_noise(seed, rows[:, None], k, vv[None, :])
+            s = z + G                                           # fp32 add
+        else:
+            raise ValueError(sampling)
+        x = np.argmax(s, axis=1)                                # step 4 (first max)
+        if choose is not None:
+            x = np.asarray(choose(k, rows, s, x), dtype=np.int64)
+        ell = conf_b + (widen(h[rows, k - 1]) @ w_h + e @ w_e)  # step 5
+        c = sigmoid64(ell / T[k - 1]).astype(np.float32)
+        S = (S * c).astype(np.float32)                          # step 6
+        tokens[:, k - 1] = x
+        zsel[:, k - 1] = z[ar, x]
+        conf[:, k - 1] = c
+        surv[:, k - 1] = S
+        if trace is not None:
+            trace.append(dict(k=k, z64=z64, z=z, s=s, e=e, ell=ell, x_prev=x_prev.copy()))
+        x_prev = x
+    return tokens, zsel, conf, surv
+
+
+# ----------------------------------------------------------------------------
+# Hardware-aware prefix scheduler
+# ----------------------------------------------------------------------------
+def schedule(surv, t_step, n_min: int):
+    """Global throughput maximisation over per-request verify lengths
+    ([P-wisp] "2. The Hardware-Aware Prefix Scheduler"; [P-blog] §6; [P-news]
+    "Confidence-scheduled verification").
+
+    Objective (reading): every request commits one token from its verify pass
+    whatever happens (the correction or bonus token), and its expected number
+    of accepted drafts is the sum of its prefix survivals over the verified
+    positions.  With n = B + M tokens in the verify step (each request's
+    anchor plus M scheduled drafts) and t_step[n - n_min] the step cost,
+    maximise  Phi(l) = (B + sum_i sum_{k <= l_i} S_{i,k}) / t_step(B + sum_i l_i)
+    over all l in {0..gamma}^B.
+
+    Survival is non-increasing along each request, so for every total M the
+    best set is the M largest gains, and that set is prefix-closed: ranking
+    all (i, k) by (S desc, i asc, k asc) and taking the top M is optimal.
+    Numerics (reading): gains are fixed point g = rint(S * 2^32) (ties to
+    even), sums are exact int64, and Phi(M) is one IEEE fp64 division of
+    (B * 2^32 + sum of the top-M gains) by t_step.  M* is the smallest M
+    attaining the largest Phi; M ranges over 0..min(B*gamma, n_max - B).
+
+    Returns (lens int32 [B], M*, objective = Phi(M*) / 2^32).
+    """
+    surv = np.asarray(surv, dtype=np.float32)
+    B, gamma = surv.shape
+    t_step = np.asarray(t_step, dtype=np.float64)
+    if n_min > B or n_min + t_step.size - 1 < B:
+        raise ValueError("step-cost table must cover n = B")
+    m_max = min(B * gamma, n_min + t_step.size - 1 - B)
+    S = surv.reshape(-1).astype(np.float64)
+    flat = np.arange(B * gamma)
+    order = np.lexsort((flat, -S))          # primary: S descending; then flat id
+    gains = np.rint(S * TWO32).astype(np.int64)
+    G = np.zeros(m_max + 1, dtype=np.int64)
+    G[1:] = np.cumsum(gains[order[:m_max]])
+    num = (np.int64(B) * np.int64(2 ** 32) + G).astype(np.float64)
+    phi = num / t_step[B + np.arange(m_max + 1) - n_min]
+    m_star = int(np.argmax(phi))            # first occurrence: smallest M
+    lens = np.bincount(order[:m_star] // gamma, minlength=B).astype(np.int32)
+    return lens, m_star, float(phi[m_star]) / TWO32
+
+
+# ----------------------------------------------------------------------------
+# Verification
+# ----------------------------------------------------------------------------
+def verify(tokens, target, lens):
+    """Strict prefix match ([P-news] opening: accepted tokens stick, the first
+    rejected token and everything after it are dropped; [P-blog] §3: the
+    target verifies the scheduled prefix).
+
+    accepted_b = number of leading scheduled drafts equal to the target's
+    tokens (scan left to right, stop at the first mismatch or at lens_b);
+    bonus_b = target[b][accepted_b], the target's own token at the first
+    rejected position, or after the last verified one.  Reading: exact token
+    match in every sampling mode."""
+    tokens = np.asarray(tokens)
+    target = np.asarray(target)
+    B = tokens.shape[0]
+    accepted = np.zeros(B, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        a = 0
+        while a < int(lens[b]) and int(tokens[b, a]) == int(target[b, a]):
+            a += 1
+        accepted[b] = a
+        bonus[b] = target[b, a]
+    return accepted, bonus
+
+
+def draft_workload(w: dict, rows=None, choose=None, trace=None, seed=None):
+    """Convenience wrapper over `draft` for a workload dictionary."""
+    cfg = w["cfg"]
+    return draft(w["anchor"], w["U"], w["h"], w["W1"], w["W2"], w["conf_w"], w["conf_b"],
+                 w["sts_T"], sampling=cfg.sampling, seed=w["seed"] if seed is None else seed,
+                 rows=rows, choose=choose, trace=trace)

@@ -1,0 +1,203 @@
+"""ctypes binding of libdspark (argument marshalling only).
+
+Every function passes device pointers of torch tensors and torch's current
+HIP stream to the C ABI declared in include/dspark.h; no step of the path is
+computed here.  If the library has not been built the first call raises
+RuntimeError: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_NAME = "libdspark.so"
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+DSPARK_OK, DSPARK_ERR_INVALID_ARG, DSPARK_ERR_UNSUPPORTED, DSPARK_ERR_WORKSPACE, DSPARK_ERR_HIP = range(5)
+DSPARK_F32, DSPARK_BF16 = 0, 1
+DSPARK_GREEDY, DSPARK_GUMBEL = 0, 1
+
+_lib = None
+_lock = threading.Lock()
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"dspark status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def _declare(lib):
+    c_int, c_size, c_vp, c_f, c_u64 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_uint64
+    lib.dspark_draft_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+    lib.dspark_draft_workspace_bytes.restype = c_size
+    lib.dspark_markov_draft.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int,
+                                        c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_vp, c_f, c_vp, c_int, c_u64,
+                                        c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]
+    lib.dspark_markov_draft.restype = c_int
+    lib.dspark_schedule.argtypes = [c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
+    lib.dspark_schedule.restype = c_int
+    lib.dspark_verify.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.dspark_verify.restype = c_int
+    lib.dspark_status_string.argtypes = [c_int]
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    lib.dspark_last_error.argtypes = []
+    lib.dspark_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (once) and return the ctypes handle of libdspark."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            p = path or library_path()
+            if not os.path.exists(p):
+                raise RuntimeError(f"{p} is not built: run __graft_entry__.build() first "
+                                   "(the HIP library is required; there is no fallback)")
+            _lib = _declare(ctypes.CDLL(p))
+        return _lib
+
+
+def _check(status: int):
+    if status != DSPARK_OK:
+        lib = load()
+        msg = lib.dspark_last_error().decode() or lib.dspark_status_string(status).decode()
+        raise DSparkError(status, msg)
+
+
+# ----------------------------------------------------------------------------
+# torch-facing wrappers
+# ----------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+_ws_cache = {}
+
+
+def workspace_bytes(B: int, gamma: int, V: int, r: int) -> int:
+    return int(load().dspark_draft_workspace_bytes(B, gamma, V, r))
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    key = (device.index if device.index is not None else torch.cuda.current_device())
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def markov_draft(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, mode: str = "greedy",
+                 seed: int = 0, out=None, workspace=None):
+    """Draft gamma tokens per request with the Markov head; returns
+    (tokens int32, logit fp32, conf fp32, surv fp32), each [B, gamma].
+
+    U [B, gamma, V], h [B, gamma, d], W1 [V, r], W2 [r, V] are all float32 or
+    all bfloat16 device tensors; anchor int32 [B]; conf_w fp32 [d + r];
+    sts_T fp32 [gamma]."""
+    torch = _torch()
+    lib = load()
+    _need(U, "U")
+    B, gamma, V = U.shape
+    dev = U.device
+    dt = U.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("U must be float32 or bfloat16")
+    r = W1.shape[1]
+    d = h.shape[2]
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(h, "h", dt, (B, gamma, d), dev)
+    _need(W1, "W1", dt, (V, r), dev)
+    _need(W2, "W2", dt, (r, V), dev)
+    _need(conf_w, "conf_w", torch.float32, (d + r,), dev)
+    _need(sts_T, "sts_T", torch.float32, (gamma,), dev)
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    tokens, logit, conf, surv = out
+    nbytes = workspace_bytes(B, gamma, V, r)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.dspark_markov_draft(
+        B, gamma, V, r, d, DSPARK_BF16 if dt == torch.bfloat16 else DSPARK_F32,
+        _ptr(anchor), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2),
+        _ptr(conf_w), ctypes.c_float(conf_b), _ptr(sts_T),
+        DSPARK_GUMBEL if mode == "gumbel" else DSPARK_GREEDY, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+        _ptr(tokens), _ptr(logit), _ptr(conf), _ptr(surv),
+        _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    _check(st)
+    return tokens, logit, conf, surv
+
+
+def schedule(surv, t_step, n_min: int, out=None):
+    """Prefix scheduler; returns (lens int32 [B], m int32 [1], objective fp64 [1])."""
+    torch = _torch()
+    lib = load()
+    _need(surv, "surv", torch.float32)
+    B, gamma = surv.shape
+    dev = surv.device
+    _need(t_step, "t_step", torch.float64, None, dev)
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.float64, device=dev))
+    lens, m, obj = out
+    st = lib.dspark_schedule(B, gamma, _ptr(surv), _ptr(t_step), int(n_min), int(t_step.numel()),
+                             _ptr(lens), _ptr(m), _ptr(obj), _stream())
+    _check(st)
+    return lens, m, obj
+
+
+def verify(tokens, target, lens, out=None):
+    """Prefix-match verify; returns (accepted int32 [B], bonus int32 [B])."""
+    torch = _torch()
+    lib = load()
+    _need(tokens, "tokens", torch.int32)
+    B, gamma = tokens.shape
+    dev = tokens.device
+    _need(target, "target", torch.int32, (B, gamma + 1), dev)
+    _need(lens, "lens", torch.int32, (B,), dev)
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    acc, bonus = out
+    st = lib.dspark_verify(B, gamma, _ptr(tokens), _ptr(target), _ptr(lens),
+                           _ptr(acc), _ptr(bonus), _stream())
+    _check(st)
+    return acc, bonus
