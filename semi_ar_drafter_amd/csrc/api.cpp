@@ -1,0 +1,141 @@
+// C ABI of libdspark (declared in include/dspark.h): host-side argument
+// validation, workspace sizing, status reporting and dispatch to the HIP
+// launchers.  Every check runs before anything is enqueued, so argument
+// errors are reported synchronously and without touching the GPU.
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dspark.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dspark_status fail(dspark_status s, const char* fmt, const char* detail = nullptr) {
+  if (detail)
+    std::snprintf(g_last_error, sizeof g_last_error, fmt, detail);
+  else
+    std::snprintf(g_last_error, sizeof g_last_error, "%s", fmt);
+  return s;
+}
+
+dspark_status hip_fail(hipError_t e) {
+  std::snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", int(e), hipGetErrorString(e));
+  return DSPARK_ERR_HIP;
+}
+
+constexpr int kMaxGamma = 64;
+constexpr int kMaxD = 65536;
+constexpr int kMaxV = 1 << 24;
+
+}  // namespace
+
+extern "C" {
+
+const char* dspark_status_string(dspark_status s) {
+  switch (s) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_INVALID_ARG: return "invalid argument";
+    case DSPARK_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case DSPARK_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case DSPARK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dspark_last_error(void) { return g_last_error; }
+
+size_t dspark_draft_workspace_bytes(int B, int gamma, int V, int r) {
+  (void)V;
+  (void)r;
+  if (B <= 0 || gamma <= 0) return 0;
+  return dspark::draft_workspace_layout(B, gamma).total;
+}
+
+dspark_status dspark_markov_draft(int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+                                  const int32_t* anchor, const void* U, const void* h, const void* W1,
+                                  const void* W2, const float* conf_w, float conf_b, const float* sts_T,
+                                  dspark_sampling mode, uint64_t seed, int32_t* tokens, float* logit,
+                                  float* conf, float* surv, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || gamma < 0 || V < 0 || r < 0 || d < 0)
+    return fail(DSPARK_ERR_INVALID_ARG, "negative size");
+  if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_INVALID_ARG, "unknown dtype");
+  if (mode != DSPARK_GREEDY && mode != DSPARK_GUMBEL) return fail(DSPARK_ERR_INVALID_ARG, "unknown sampling mode");
+  if (B == 0 || gamma == 0) return DSPARK_OK;
+  if (V < 1 || r < 1) return fail(DSPARK_ERR_INVALID_ARG, "V and r must be positive");
+  if (!anchor || !U || !W1 || !W2 || !conf_w || !sts_T || !tokens || !logit || !conf || !surv ||
+      (d > 0 && !h))
+    return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  if (gamma > kMaxGamma) return fail(DSPARK_ERR_UNSUPPORTED, "gamma > 64");
+  if (d > kMaxD) return fail(DSPARK_ERR_UNSUPPORTED, "d > 65536");
+  if (V > kMaxV) return fail(DSPARK_ERR_UNSUPPORTED, "V > 2^24");
+  const int elem = dtype == DSPARK_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(U) % elem ||
+      reinterpret_cast<uintptr_t>(W2) % elem || (h && reinterpret_cast<uintptr_t>(h) % elem))
+    return fail(DSPARK_ERR_INVALID_ARG, "misaligned tensor (W1 needs 16-byte alignment)");
+  const size_t need = dspark_draft_workspace_bytes(B, gamma, V, r);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSPARK_ERR_WORKSPACE, "workspace missing or smaller than dspark_draft_workspace_bytes()");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(DSPARK_ERR_WORKSPACE, "workspace not 256-byte aligned");
+
+  dspark::DraftArgs a;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.r = r;
+  a.d = d;
+  a.bf16 = dtype == DSPARK_BF16;
+  a.gumbel = mode == DSPARK_GUMBEL;
+  a.seed = seed;
+  a.anchor = anchor;
+  a.U = U;
+  a.h = h;
+  a.W1 = W1;
+  a.W2 = W2;
+  a.conf_w = conf_w;
+  a.conf_b = conf_b;
+  a.sts_T = sts_T;
+  a.tokens = tokens;
+  a.logit = logit;
+  a.conf = conf;
+  a.surv = surv;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  const char* why = nullptr;
+  hipError_t e = dspark::launch_markov_draft(a, stream, &why);
+  if (why) return fail(DSPARK_ERR_UNSUPPORTED, "%s", why);
+  if (e != hipSuccess) return hip_fail(e);
+  return DSPARK_OK;
+}
+
+dspark_status dspark_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min, int n_count,
+                              int32_t* lens, int32_t* m_out, double* objective, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || gamma < 0 || n_count < 1) return fail(DSPARK_ERR_INVALID_ARG, "negative size or empty step-cost table");
+  if (!t_step || !m_out || (B > 0 && (!lens || (gamma > 0 && !surv))))
+    return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  if (n_min > B || (long long)n_min + n_count - 1 < B)
+    return fail(DSPARK_ERR_INVALID_ARG, "step-cost table must cover n = B (n_min <= B <= n_min + n_count - 1)");
+  if ((long long)B * gamma > dspark::kMaxScheduleItems)
+    return fail(DSPARK_ERR_UNSUPPORTED, "B * gamma > 16384");
+  hipError_t e = dspark::launch_schedule(B, gamma, surv, t_step, n_min, n_count, lens, m_out, objective, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return DSPARK_OK;
+}
+
+dspark_status dspark_verify(int B, int gamma, const int32_t* tokens, const int32_t* target, const int32_t* lens,
+                            int32_t* accepted, int32_t* bonus, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || gamma < 0) return fail(DSPARK_ERR_INVALID_ARG, "negative size");
+  if (B == 0) return DSPARK_OK;
+  if (!target || !lens || !accepted || !bonus || (gamma > 0 && !tokens))
+    return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  hipError_t e = dspark::launch_verify(B, gamma, tokens, target, lens, accepted, bonus, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return DSPARK_OK;
+}
+
+}  // extern "C"

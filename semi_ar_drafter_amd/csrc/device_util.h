@@ -1,0 +1,99 @@
+// Device helpers shared by the libdspark kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// bfloat16 is the upper half of an IEEE fp32: widening is a 16-bit shift.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// Order-preserving map of an fp32 value to uint32 (larger value -> larger
+// code); -0 is folded onto +0 so that equal values compare equal.
+__device__ __forceinline__ uint32_t ord_f32(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Argmax key: the larger key has the larger value, and among equal values
+// the smaller index.  Key 0 means "no candidate".
+__device__ __forceinline__ uint64_t argmax_key(float s, uint32_t idx) {
+  return (uint64_t(ord_f32(s)) << 32) | uint64_t(~idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~uint32_t(key); }
+__device__ __forceinline__ float key_value(uint64_t key) { return unord_f32(uint32_t(key >> 32)); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  uint32_t lo = __shfl_xor(uint32_t(x), m, 64);
+  uint32_t hi = __shfl_xor(uint32_t(x >> 32), m, 64);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64-bit
+// multiplies on counter words 0 and 2 with the result words crossed and
+// xor-ed with the key; the key advances by the Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                              uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
+    uint32_t hi0 = __umulhi(m0, c0), lo0 = m0 * c0;
+    uint32_t hi1 = __umulhi(m1, c2), lo1 = m1 * c2;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// Standard Gumbel sample from one 32-bit hash word: u = (2*(w>>9)+1) * 2^-24
+// lies in (0, 1) and is exact in fp32; G = -ln(-ln u).
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+  float u = float((w >> 9) * 2u + 1u) * 0x1p-24f;
+  return -logf(-logf(u));
+}
+
+// Grid-wide barrier for a co-resident (cooperatively launched) grid.  The
+// counter counts arrivals over the whole launch; barrier number n waits
+// until n * gridDim.x arrivals.  A bounded spin: after `limit` polls the
+// error flag is raised and every later barrier returns at once, so every
+// wave always reaches the end of the kernel.
+__device__ __forceinline__ void grid_barrier(unsigned int* counter, unsigned int* err,
+                                             unsigned int target, unsigned int limit) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned int polls = 0;
+    while (__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+      if (++polls > limit) {
+        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  __threadfence();
+}
+
+}  // namespace dspark

@@ -1,0 +1,49 @@
+// Host-side launch interface between the C ABI layer (api.cpp) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// Upper bound on the draft kernel's grid (one workgroup per compute unit).
+constexpr int kMaxDraftWorkgroups = 512;
+// Largest number of requests one workgroup can own for the confidence epilogue.
+constexpr int kMaxOwnedRows = 64;
+// Scheduler: one workgroup sorts all (request, position) keys in LDS.
+constexpr int kMaxScheduleItems = 16384;
+
+struct DraftArgs {
+  int B, gamma, V, r, d;
+  bool bf16, gumbel;
+  uint64_t seed;
+  const int32_t* anchor;
+  const void *U, *h, *W1, *W2;
+  const float* conf_w;
+  float conf_b;
+  const float* sts_T;
+  int32_t* tokens;
+  float *logit, *conf, *surv;
+  void* ws;
+  size_t ws_bytes;
+};
+
+// Workspace carve-up of the draft call (byte offsets, 256-aligned).
+struct DraftWorkspace {
+  size_t ctrl, slots, zpart, hdot, total;
+};
+DraftWorkspace draft_workspace_layout(int B, int gamma);
+
+// Returns hipSuccess or the first HIP error; sets *unsupported (with a reason)
+// when the shape is outside what the kernels handle.
+hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported);
+
+hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min,
+                           int n_count, int32_t* lens, int32_t* m_out, double* objective,
+                           hipStream_t stream);
+
+hipError_t launch_verify(int B, int gamma, const int32_t* tokens, const int32_t* target,
+                         const int32_t* lens, int32_t* accepted, int32_t* bonus, hipStream_t stream);
+
+}  // namespace dspark

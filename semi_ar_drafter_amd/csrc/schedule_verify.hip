@@ -1,0 +1,179 @@
+// Hardware-aware prefix scheduler and prefix-match verify for gfx950.
+//
+// Scheduler ("DSpark: Overcoming the Efficiency Wall in LLM Speculative
+// Decoding", "2. The Hardware-Aware Prefix Scheduler"; "DSpark: DeepSeek's
+// new speculative decoding work", §6): choose per-request verify lengths
+// maximising (B + sum of scheduled survivals) / t_step(B + M).  Survival is
+// non-increasing along each request, so the best set of M drafts is the top
+// M by (S desc, request asc, position asc) and only M has to be searched.
+// One workgroup of 1024 threads: bitonic sort of 64-bit keys in LDS, a
+// block scan of fixed-point gains, one fp64 division per candidate M, a
+// block arg-max, and a per-request count below the M*-th key.
+//
+// Verify ("DeepSeek's DSpark just fixed the two things that held back faster
+// AI inference", opening; "DSpark: DeepSeek's new speculative decoding
+// work", §3): longest matching prefix of the scheduled drafts and the
+// target's token right after it.
+#include "device_util.h"
+#include "launch.h"
+
+namespace dspark {
+namespace {
+
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedWaves = kSchedThreads / 64;
+
+// Sort key: ascending key order = descending survival, then ascending flat
+// index (request-major), so the first M keys are the scheduler's top M.
+__device__ __forceinline__ uint64_t sched_key(float s, uint32_t flat) {
+  return (uint64_t(~ord_f32(s)) << 32) | uint64_t(flat);
+}
+__device__ __forceinline__ long long gain_fixed(uint64_t key) {
+  const float s = unord_f32(~uint32_t(key >> 32));
+  return (long long)rint(double(s) * 4294967296.0);
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamma, const float* __restrict__ surv,
+                                                                 const double* __restrict__ t_step, int n_min,
+                                                                 int n_count, int32_t* lens, int32_t* m_out,
+                                                                 double* objective) {
+  __shared__ uint64_t keys[kMaxScheduleItems];
+  __shared__ long long wave_tot[kSchedWaves];
+  __shared__ double red_phi[kSchedWaves];
+  __shared__ int red_m[kSchedWaves];
+  __shared__ uint64_t s_tau;
+  __shared__ int s_mstar;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = B * gamma;
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+
+  for (int i = tid; i < n2; i += kSchedThreads)
+    keys[i] = (i < n) ? sched_key(surv[i], uint32_t(i)) : ~0ull;
+
+  // bitonic sort, ascending
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int t = tid; t < (n2 >> 1); t += kSchedThreads) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t a = keys[lo], b = keys[hi];
+        if ((a > b) == up) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // M ranges over 0..m_max; thread t scans positions [t*C, (t+1)*C).
+  const int m_max = min(n, n_min + n_count - 1 - B);
+  const int C = (m_max + kSchedThreads - 1) / kSchedThreads;
+  const int p0 = min(tid * C, m_max), p1 = min(p0 + C, m_max);
+  long long local = 0;
+  for (int p = p0; p < p1; ++p) local += gain_fixed(keys[p]);
+  // block exclusive scan of the per-thread sums
+  long long incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  long long before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_tot[w];
+  long long G = before + incl - local;   // sum of gains at positions < p0
+
+  const long long base = (long long)B << 32;
+  double best = -INFINITY;
+  int best_m = 0x7FFFFFFF;
+  if (tid == 0) {
+    best = double(base) / t_step[B - n_min];
+    best_m = 0;
+  }
+  for (int p = p0; p < p1; ++p) {
+    G += gain_fixed(keys[p]);
+    const int M = p + 1;
+    const double phi = double(base + G) / t_step[B + M - n_min];
+    if (phi > best) {
+      best = phi;
+      best_m = M;
+    }
+  }
+  // block arg-max: larger phi, then smaller M
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const double ob = __shfl_xor(best, m, 64);
+    const int om = __shfl_xor(best_m, m, 64);
+    if (ob > best || (ob == best && om < best_m)) {
+      best = ob;
+      best_m = om;
+    }
+  }
+  if (lane == 0) {
+    red_phi[wave] = best;
+    red_m[wave] = best_m;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double bb = red_phi[0];
+    int bm = red_m[0];
+    for (int w = 1; w < kSchedWaves; ++w)
+      if (red_phi[w] > bb || (red_phi[w] == bb && red_m[w] < bm)) {
+        bb = red_phi[w];
+        bm = red_m[w];
+      }
+    s_mstar = bm;
+    s_tau = (bm < n) ? keys[bm] : ~0ull;
+    m_out[0] = bm;
+    if (objective) objective[0] = bb / 4294967296.0;
+  }
+  __syncthreads();
+  const uint64_t tau = s_tau;
+  for (int b = tid; b < B; b += kSchedThreads) {
+    int cnt = 0;
+    for (int k = 0; k < gamma; ++k) {
+      const int i = b * gamma + k;
+      cnt += sched_key(surv[i], uint32_t(i)) < tau ? 1 : 0;
+    }
+    lens[b] = cnt;
+  }
+}
+
+__global__ __launch_bounds__(256) void verify_kernel(int B, int gamma, const int32_t* __restrict__ tokens,
+                                                     const int32_t* __restrict__ target,
+                                                     const int32_t* __restrict__ lens, int32_t* accepted,
+                                                     int32_t* bonus) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int L = min(max(int(lens[b]), 0), gamma);
+  const int32_t* tk = tokens + size_t(b) * gamma;
+  const int32_t* tg = target + size_t(b) * (gamma + 1);
+  int a = 0;
+  while (a < L && tk[a] == tg[a]) ++a;
+  accepted[b] = a;
+  bonus[b] = tg[a];
+}
+
+}  // namespace
+
+hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min, int n_count,
+                           int32_t* lens, int32_t* m_out, double* objective, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, B, gamma, surv, t_step, n_min,
+                     n_count, lens, m_out, objective);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(int B, int gamma, const int32_t* tokens, const int32_t* target, const int32_t* lens,
+                         int32_t* accepted, int32_t* bonus, hipStream_t stream) {
+  hipLaunchKernelGGL(verify_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, gamma, tokens, target, lens,
+                     accepted, bonus);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

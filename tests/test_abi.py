@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments on the host before touching the GPU (CPU only: no compute call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from semi_ar_drafter_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from semi_ar_drafter_amd import build_lib
+        build_lib.build(verbose=False)
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"dspark_markov_draft", "dspark_schedule", "dspark_verify"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dspark_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+# fake, suitably aligned device addresses: never dereferenced by failing calls
+P = ctypes.c_void_p(0x10000)
+NULL = ctypes.c_void_p(0)
+
+
+def draft(lib, B=4, gamma=4, V=1024, r=32, d=16, dtype=1, mode=0, ws=P, ws_bytes=None, **over):
+    ptrs = dict(anchor=P, U=P, h=P, W1=P, W2=P, conf_w=P, sts_T=P, tokens=P, logit=P, conf=P, surv=P)
+    ptrs.update(over)
+    if ws_bytes is None:
+        ws_bytes = lib.dspark_draft_workspace_bytes(max(B, 1), max(gamma, 1), V, r)
+    return lib.dspark_markov_draft(B, gamma, V, r, d, dtype, ptrs["anchor"], ptrs["U"], ptrs["h"], ptrs["W1"],
+                                   ptrs["W2"], ptrs["conf_w"], ctypes.c_float(1.0), ptrs["sts_T"], mode,
+                                   ctypes.c_uint64(0), ptrs["tokens"], ptrs["logit"], ptrs["conf"], ptrs["surv"],
+                                   ws, ctypes.c_size_t(ws_bytes), NULL)
+
+
+def test_draft_validation(lib):
+    assert draft(lib, B=-1) == INVALID
+    assert draft(lib, V=-3) == INVALID
+    assert draft(lib, dtype=7) == INVALID
+    assert draft(lib, mode=3) == INVALID
+    assert draft(lib, V=0) == INVALID
+    for name in ("anchor", "U", "W1", "W2", "conf_w", "sts_T", "tokens", "logit", "conf", "surv", "h"):
+        assert draft(lib, **{name: NULL}) == INVALID, name
+    assert draft(lib, gamma=65) == UNSUPPORTED
+    assert draft(lib, d=70000) == UNSUPPORTED
+    assert draft(lib, r=48) == UNSUPPORTED                # bf16 needs r in {32, 64, 128, 256}
+    assert draft(lib, dtype=0, r=256) == UNSUPPORTED      # fp32 needs r in {16, 32, 64}
+    assert draft(lib, W1=ctypes.c_void_p(0x10008)) == INVALID   # W1 rows read 16 bytes at a time
+    assert draft(lib, ws=NULL) == WORKSPACE
+    assert draft(lib, ws_bytes=100) == WORKSPACE
+    assert draft(lib, ws=ctypes.c_void_p(0x10040)) == WORKSPACE  # not 256-byte aligned
+    assert lib.dspark_last_error().decode() != ""
+    # empty batches are valid no-ops and need no pointers at all
+    assert draft(lib, B=0, anchor=NULL, U=NULL, ws=NULL, ws_bytes=0) == OK
+    assert draft(lib, gamma=0, anchor=NULL, U=NULL, ws=NULL, ws_bytes=0) == OK
+
+
+def test_workspace_size(lib):
+    assert lib.dspark_draft_workspace_bytes(0, 16, 151936, 256) == 0
+    a = lib.dspark_draft_workspace_bytes(256, 16, 151936, 256)
+    b = lib.dspark_draft_workspace_bytes(512, 16, 151936, 256)
+    assert a % 256 == 0 and b % 256 == 0 and b > a > 256 * 16 * 8
+
+
+def sched(lib, B=4, gamma=4, n_min=4, n_count=17, surv=P, t=P, lens=P, m=P):
+    return lib.dspark_schedule(B, gamma, surv, t, n_min, n_count, lens, m, NULL, NULL)
+
+
+def test_schedule_validation(lib):
+    assert sched(lib, B=-1) == INVALID
+    assert sched(lib, n_count=0) == INVALID
+    assert sched(lib, n_min=5) == INVALID                 # table starts above B
+    assert sched(lib, n_min=0, n_count=4) == INVALID      # table ends below B
+    assert sched(lib, surv=NULL) == INVALID
+    assert sched(lib, t=NULL) == INVALID
+    assert sched(lib, lens=NULL) == INVALID
+    assert sched(lib, m=NULL) == INVALID
+    assert sched(lib, B=1025, gamma=16, n_min=1025, n_count=16401) == UNSUPPORTED
+
+
+def test_verify_validation(lib):
+    v = lambda B=4, g=4, tk=P, tg=P, ln=P, a=P, bo=P: lib.dspark_verify(B, g, tk, tg, ln, a, bo, NULL)
+    assert v(B=-2) == INVALID
+    assert v(g=-1) == INVALID
+    assert v(tk=NULL) == INVALID
+    assert v(tg=NULL) == INVALID
+    assert v(ln=NULL) == INVALID
+    assert v(a=NULL) == INVALID
+    assert v(bo=NULL) == INVALID
+    assert v(B=0, tk=NULL, tg=NULL) == OK
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.dspark_status_string(s).decode()
+    assert lib.dspark_status_string(99).decode() == "unknown status"
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Token ids, scheduled lengths and verify outputs are
+bit-exact; logits within 1e-2, confidences and survivals within 1e-4; near
+ties (oracle top-2 gap < 2e-2) replay the GPU's token in the oracle.
+
+Small cases span several vocabulary tiles, several request tiles, two
+request groups and ragged tails; the full-size configurations run in the
+launch configuration the benchmark times and compare sampled requests (every
+request's chain is independent, so the oracle can compute any subset).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from oracle import dspark_oracle as orc  # noqa: E402
+from semi_ar_drafter_amd import workloads as wl  # noqa: E402
+
+from parity import check_draft, gpu_draft, to_device  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from semi_ar_drafter_amd import binding
+    binding.load()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(w, rows=None, expect_some_replays=False):
+    cfg = w["cfg"]
+    say(f"[case] {cfg.name} B={cfg.B} gamma={cfg.gamma} V={cfg.V} r={cfg.r} d={cfg.d} "
+        f"{cfg.dtype} {cfg.sampling} seed={w['seed']}")
+    d = to_device(w)
+    out = gpu_draft(d)
+    st = check_draft(w, out, rows=rows)
+    say(f"  replays={st.replays} mismatches={st.mismatches} first={st.first_mismatch} "
+        f"dlogit={st.max_dlogit:.2e} dconf={st.max_dconf:.2e} dsurv={st.max_dsurv:.2e}")
+    assert st.ok(), st
+    tok, logit, conf, surv = out
+    assert ((tok >= 0) & (tok < cfg.V)).all()
+    assert (np.diff(surv, axis=1) <= 0).all() and ((surv >= 0) & (surv <= 1)).all()
+    return d, out
+
+
+def gpu_schedule(d, surv_np):
+    from semi_ar_drafter_amd import schedule
+    surv = torch.from_numpy(surv_np).to("cuda:0")
+    lens, m, obj = schedule(surv, d["t_step"], d["n_min"])
+    torch.cuda.synchronize()
+    return lens.cpu().numpy(), int(m.cpu()[0]), float(obj.cpu()[0])
+
+
+def gpu_verify(tok_np, target_np, lens_np):
+    from semi_ar_drafter_amd import verify
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+    acc, bonus = verify(dev(tok_np), dev(target_np), dev(lens_np))
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), bonus.cpu().numpy()
+
+
+def end_to_end(w, d, out):
+    """Scheduler and verify on identical inputs (the GPU's own draft outputs)."""
+    tok, _, _, surv = out
+    lens, m, obj = gpu_schedule(d, surv)
+    o_lens, o_m, o_obj = orc.schedule(surv, w["t_step"], w["n_min"])
+    assert m == o_m and (lens == o_lens).all() and obj == o_obj
+    acc, bonus = gpu_verify(tok, w["target"], lens)
+    o_acc, o_bonus = orc.verify(tok, w["target"], lens)
+    assert (acc == o_acc).all() and (bonus == o_bonus).all()
+    say(f"  schedule M*={m} objective={obj:.6f} mean accepted={acc.mean():.3f}")
+    return lens, acc, bonus
+
+
+# --------------------------------------------------------------------------
+# small cases: whole batch against the oracle
+# --------------------------------------------------------------------------
+def test_tiny_fp32_config():
+    w = wl.make_workload(wl.CONFIGS[0])
+    d, out = run_case(w)
+    end_to_end(w, d, out)
+
+
+SMALL = [
+    dict(B=37, gamma=5, V=1000, r=64, d=100, dtype="bf16"),            # ragged V tile, ragged request tile
+    dict(B=300, gamma=3, V=4099, r=32, d=33, dtype="bf16"),            # two request groups, V % 4 != 0
+    dict(B=16, gamma=4, V=8192, r=256, d=64, dtype="bf16"),            # full rank, exact tiles
+    dict(B=5, gamma=6, V=2051, r=128, d=8, dtype="bf16"),
+    dict(B=9, gamma=4, V=777, r=16, d=20, dtype="f32"),
+    dict(B=33, gamma=3, V=3000, r=64, d=40, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(str(v) for v in s.values()))
+def test_small_greedy(shape):
+    w = wl.make_workload(wl.small_config(**shape))
+    d, out = run_case(w)
+    end_to_end(w, d, out)
+
+
+@pytest.mark.parametrize("shape", [dict(B=20, gamma=4, V=3000, r=64, d=32, dtype="bf16"),
+                                   dict(B=7, gamma=5, V=1234, r=32, d=16, dtype="f32")],
+                         ids=["bf16", "f32"])
+def test_small_gumbel(shape):
+    cfg = wl.small_config(sampling="gumbel", **shape)
+    w = wl.make_workload(cfg)
+    w["seed"] = 0x123456789AB
+    d, out = run_case(w)
+    end_to_end(w, d, out)
+
+
+def test_small_weak_plant_many_near_ties():
+    """No plant: logits are pure noise, so near ties and replays are routine."""
+    cfg = wl.small_config(B=64, gamma=4, V=20000, r=64, d=16, dtype="bf16", plant=(0.0, 0.0))
+    w = wl.make_workload(cfg)
+    run_case(w)
+
+
+def test_out_of_range_anchors_are_clamped():
+    cfg = wl.small_config(B=6, gamma=3, V=500, r=32, d=8, dtype="bf16")
+    w = wl.make_workload(cfg)
+    bad = w["anchor"].copy()
+    bad[:3] = [-7, 500, 10 ** 6]
+    w["anchor"] = bad
+    d = to_device(w)
+    out = gpu_draft(d)
+    w_ref = dict(w, anchor=np.clip(bad, 0, cfg.V - 1).astype(np.int32))
+    st = check_draft(w_ref, out)
+    assert st.ok(), st
+
+
+def test_determinism_bitwise():
+    w = wl.make_workload(wl.small_config(B=70, gamma=4, V=5000, r=64, d=24, dtype="bf16"))
+    d = to_device(w)
+    a = gpu_draft(d)
+    b = gpu_draft(d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_empty_batch_is_noop():
+    from semi_ar_drafter_amd import markov_draft
+    w = wl.make_workload(wl.small_config(B=0, gamma=4, V=256, r=32, d=8, dtype="bf16"))
+    d = to_device(w)
+    tok, logit, conf, surv = markov_draft(d["anchor"], d["U"], d["h"], d["W1"], d["W2"], d["conf_w"],
+                                          1.0, d["sts_T"])
+    assert tok.shape == (0, 4)
+
+
+# --------------------------------------------------------------------------
+# scheduler and verify alone, on random inputs
+# --------------------------------------------------------------------------
+def _rand_surv(rng, B, g, mode):
+    if mode == "ties":
+        c = np.array([1.0, 0.5, 0.25, 0.0], np.float32)[rng.integers(0, 4, size=(B, g))]
+    elif mode == "saturated":
+        c = np.where(rng.random((B, g)) < 0.7, 1.0, rng.random((B, g)) * 1e-6).astype(np.float32)
+    else:
+        c = rng.random((B, g)).astype(np.float32)
+    S = np.cumprod(c, axis=1, dtype=np.float32)
+    for k in range(1, g):       # exact fp32 running product
+        S[:, k] = (S[:, k - 1] * c[:, k]).astype(np.float32)
+    return S
+
+
+@pytest.mark.parametrize("B,g", [(1, 1), (3, 5), (64, 16), (256, 16), (512, 16), (1024, 16), (100, 3)])
+@pytest.mark.parametrize("mode", ["random", "ties", "saturated"])
+def test_schedule_parity(B, g, mode):
+    rng = np.random.default_rng(B * 131 + g * 7 + len(mode))
+    S = _rand_surv(rng, B, g, mode)
+    for table in ("linear", "quad"):
+        n = np.arange(B, B + B * g + 1, dtype=np.float64)
+        t = 1.0 + 0.01 * n if table == "linear" else 4.0 + 0.02 * n + 2e-5 * n * n
+        d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=B)
+        lens, m, obj = gpu_schedule(d, S)
+        o_lens, o_m, o_obj = orc.schedule(S, t, B)
+        assert m == o_m and (lens == o_lens).all() and obj == o_obj, (table, m, o_m)
+
+
+def test_schedule_table_offset_and_short_table():
+    rng = np.random.default_rng(3)
+    S = _rand_surv(rng, 40, 8, "random")
+    n_min = 10
+    t = 2.0 + 0.05 * np.arange(n_min, 40 + 100, dtype=np.float64)   # covers M <= 99 only
+    d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=n_min)
+    lens, m, obj = gpu_schedule(d, S)
+    o_lens, o_m, o_obj = orc.schedule(S, t, n_min)
+    assert m == o_m and (lens == o_lens).all() and obj == o_obj
+
+
+def test_verify_parity_random():
+    rng = np.random.default_rng(9)
+    for B, g, V in [(1, 1, 2), (1000, 16, 3), (513, 7, 2), (64, 16, 5)]:
+        tok = rng.integers(0, V, size=(B, g)).astype(np.int32)
+        tgt = rng.integers(0, V, size=(B, g + 1)).astype(np.int32)
+        lens = rng.integers(-2, g + 3, size=B).astype(np.int32)     # out-of-range lengths are clamped
+        acc, bonus = gpu_verify(tok, tgt, lens)
+        o_acc, o_bonus = orc.verify(tok, tgt, np.clip(lens, 0, g))
+        assert (acc == o_acc).all() and (bonus == o_bonus).all()
+
+
+# --------------------------------------------------------------------------
+# full-size configurations
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cid,nrows", [(1, None), (2, 16), (3, 12), (4, 3)])
+def test_full_size_config(cid, nrows):
+    cfg = wl.CONFIGS[cid]
+    say(f"[gen] config {cid} ...")
+    w = wl.make_workload(cfg)
+    rows = None
+    if nrows is not None:
+        rng = np.random.default_rng(cid)
+        rows = np.sort(np.concatenate([[0, cfg.B - 1], rng.choice(np.arange(1, cfg.B - 1), nrows - 2, replace=False)]))
+    d, out = run_case(w, rows=rows)
+    end_to_end(w, d, out)
+
+
+def test_chained_gumbel_iterations():
+    """Config 4 semantics at reduced batch: iteration t+1's anchor is
+    iteration t's bonus token and its seed is seed0 + t."""
+    cfg = wl.CONFIGS[4].replace(B=24, cid=40)
+    anchor = None
+    for it in range(4):
+        w = wl.make_workload(cfg, iteration=it, anchor=anchor)
+        d, out = run_case(w)
+        lens, acc, bonus = end_to_end(w, d, out)
+        anchor = bonus
