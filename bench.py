@@ -1,0 +1,182 @@
+"""Benchmark of the DSpark Markov-head draft -> prefix schedule -> verify path
+on one MI355X.
+
+One step = one pass of the whole path over one batch: dspark_markov_draft
+(gamma dependent Markov-head steps with the confidence epilogue), then
+dspark_schedule on the drafted survivals, then dspark_verify against the
+target tokens.  Inputs are resident in HBM before timing starts.
+
+Workload: B=256 requests, gamma=16, V=151936, r=256, d=5120, bf16 storage,
+greedy drafting, 64-point step-cost table 4 + 0.02 n + 2e-5 n^2 over
+n in [256, 4352] (synthetic inputs from the seeded generator).
+
+Prints one JSON line.  `value` = drafted tokens per second of the whole step
+(B * gamma / step time).  `roofline` rates the draft kernel against HBM
+bandwidth with its algorithmic bytes; `cpu_baseline` times the CPU oracle on
+a bounded sample of requests of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def algorithmic_bytes(cfg) -> int:
+    """Bytes the draft call must move at minimum: every base logit once, W2
+    once, one gathered W1 row and one hidden-state row per (request,
+    position), the confidence head, temperatures, anchors and the four
+    [B, gamma] outputs."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    B, g, V, r, d = cfg.B, cfg.gamma, cfg.V, cfg.r, cfg.d
+    return (B * g * V * e + r * V * e + B * g * r * e + B * g * d * e
+            + (d + r) * 4 + g * 4 + B * 4 + B * g * 16)
+
+
+def flops(cfg) -> int:
+    return 2 * cfg.B * cfg.gamma * cfg.r * cfg.V
+
+
+def cpu_baseline(w, rows: int):
+    """The oracle as it stands, drafting the first `rows` requests through all
+    gamma steps (requests are independent, so this is a fixed fraction of
+    the call's work)."""
+    import numpy as np
+    from oracle import dspark_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    tok, logit, conf, surv = orc.draft_workload(w, rows=np.arange(rows))
+    t1 = time.perf_counter()
+    return dict(seconds=t1 - t0, tokens=rows * w["cfg"].gamma, threads=threads)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload id (default: the B=256 configuration)")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="requests in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU only (asked for --gpus {args.gpus}); "
+              "see the design notes for how it would shard across GPUs.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from semi_ar_drafter_amd import markov_draft, schedule, verify
+    from semi_ar_drafter_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = wl.CONFIGS[args.config]
+    t_gen = time.perf_counter()
+    w = wl.make_workload(cfg)
+    print(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    anchor, U, h, W1, W2 = dev(w["anchor"]), dev(w["U"]), dev(w["h"]), dev(w["W1"]), dev(w["W2"])
+    conf_w, sts_T, target, t_step = dev(w["conf_w"]), dev(w["sts_T"]), dev(w["target"]), dev(w["t_step"])
+    B, g = cfg.B, cfg.gamma
+    outs = (torch.empty((B, g), dtype=torch.int32, device="cuda"),
+            torch.empty((B, g), dtype=torch.float32, device="cuda"),
+            torch.empty((B, g), dtype=torch.float32, device="cuda"),
+            torch.empty((B, g), dtype=torch.float32, device="cuda"))
+    sched_out = (torch.empty(B, dtype=torch.int32, device="cuda"), torch.empty(1, dtype=torch.int32, device="cuda"),
+                 torch.empty(1, dtype=torch.float64, device="cuda"))
+    ver_out = (torch.empty(B, dtype=torch.int32, device="cuda"), torch.empty(B, dtype=torch.int32, device="cuda"))
+    mode, seed = cfg.sampling, w["seed"]
+
+    def step(ev0=None, ev1=None):
+        if ev0 is not None:
+            ev0.record()
+        tok, logit, conf, surv = markov_draft(anchor, U, h, W1, W2, conf_w, w["conf_b"], sts_T, mode=mode,
+                                              seed=seed, out=outs)
+        if ev1 is not None:
+            ev1.record()
+        lens, m, obj = schedule(surv, t_step, w["n_min"], out=sched_out)
+        verify(tok, target, lens, out=ver_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(*ev[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(stop) / K
+    draft_ms = [a.elapsed_time(b) for a, b in ev]
+    draft_avg = sum(draft_ms) / K
+    value = B * g / (ms_step / 1e3)
+
+    abytes = algorithmic_bytes(cfg)
+    achieved = abytes / (draft_avg / 1e3) / 1e9
+    tflops = flops(cfg) / (draft_avg / 1e3) / 1e12
+    print(f"[bench] step {ms_step * 1e3:.1f} us, draft {draft_avg * 1e3:.1f} us "
+          f"(min {min(draft_ms) * 1e3:.1f}), {achieved:.0f} GB/s algorithmic, {tflops:.0f} TFLOP/s, "
+          f"wall {wall:.3f}s", file=sys.stderr, flush=True)
+
+    result = {
+        "metric": "drafted tokens/s at V=151936 r=256 gamma=16 B=256; % of HBM roofline",
+        "value": round(value, 1),
+        "unit": "drafted tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": "markov-draft+schedule+verify", "B": B, "gamma": g, "V": cfg.V, "r": cfg.r,
+                   "d": cfg.d, "storage": cfg.dtype, "sampling": cfg.sampling,
+                   "sps_table": "64-point 4+0.02n+2e-5n^2, n in [256, 4352]"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "markov_draft (per dspark_markov_draft call)",
+                     "algorithmic_bytes_per_launch": abytes, "launch_us": round(draft_avg * 1e3, 2)},
+        "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, args.cpu_rows)
+        result["cpu_baseline"] = {"value": round(cb["tokens"] / cb["seconds"], 2), "unit": "drafted tokens/s",
+                                  "cores": cb["threads"], "kind": "oracle",
+                                  "sample": f"first {args.cpu_rows} of {B} requests, all {g} draft steps "
+                                            f"({cb['seconds']:.1f}s, host has {os.cpu_count()} CPUs)"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -99,7 +99,13 @@ size_t dspark_draft_workspace_bytes(int B, int gamma, int V, int r);
  *   conf    fp32  [B][gamma] out     c_k
  *   surv    fp32  [B][gamma] out     S_k
  *   workspace     >= dspark_draft_workspace_bytes(B, gamma, V, r) bytes,
- *                 256-byte aligned; contents on entry are ignored
+ *                 256-byte aligned, zero-filled before its first use (e.g.
+ *                 hipMemsetAsync).  Every call leaves it zero-filled again,
+ *                 so it can be reused without clearing.  A workspace found
+ *                 dirty is cleaned by the call, whose tokens are then all -1.
+ * The call is one kernel launch.  If the kernel cannot synchronise its
+ * workgroups (it never can deadlock: its waits are bounded) every token of
+ * the call is -1.
  * Limits: gamma <= 64, d <= 65536, V <= 2^24 and V small enough that the
  * GPU's compute units can hold W2 on chip (V <= 163840 on MI355X);
  * otherwise DSPARK_ERR_UNSUPPORTED.

@@ -117,7 +117,8 @@ def _workspace(nbytes: int, device):
     key = (device.index if device.index is not None else torch.cuda.current_device())
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        # zero-filled once; every completed call leaves it zero-filled again
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 

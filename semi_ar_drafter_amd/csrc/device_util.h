@@ -71,29 +71,46 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
   return -logf(-logf(u));
 }
 
-// Grid-wide barrier for a co-resident (cooperatively launched) grid.  The
-// counter counts arrivals over the whole launch; barrier number n waits
-// until n * gridDim.x arrivals.  A bounded spin: after `limit` polls the
-// error flag is raised and every later barrier returns at once, so every
-// wave always reaches the end of the kernel.
+// Waits until this wave's outstanding vector-memory operations (loads,
+// stores, atomics) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Device-scope (all XCDs) accesses: they bypass the non-coherent caches, so
+// no L2 write-back or invalidation is needed around them.
+template <typename T>
+__device__ __forceinline__ T load_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void store_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Grid-wide barrier for a co-resident (cooperatively launched) grid whose
+// cross-workgroup data moves only through device-scope atomics, loads and
+// stores: every wave waits for its own memory operations to complete, the
+// workgroup synchronises, and one thread arrives on the counter and polls
+// it.  The counter counts arrivals over the whole launch; barrier number n
+// waits for n * gridDim.x arrivals.  The spin is bounded: after `limit`
+// polls the error flag is raised, and once it is raised every barrier
+// returns at once, so every wave always reaches the end of the kernel.
 __device__ __forceinline__ void grid_barrier(unsigned int* counter, unsigned int* err,
                                              unsigned int target, unsigned int limit) {
-  __threadfence();
+  wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned int polls = 0;
-    while (__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+    while (load_dev(counter) < target) {
+      if (load_dev(err) != 0u) break;
       if (++polls > limit) {
-        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_dev(err, 1u);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
-  __threadfence();
 }
 
 }  // namespace dspark

@@ -25,7 +25,13 @@
 //    lowest index win ties), followed by one grid barrier per step.
 //  * The confidence epilogue of request b runs in workgroup b mod grid, off
 //    the critical path; the hidden-state half of its dot product does not
-//    depend on the drafted tokens and is precomputed by draft_init_kernel.
+//    depend on the drafted tokens and is computed in the kernel's prologue.
+//  * Cross-workgroup data (argmax slots, per-workgroup winner logits, the
+//    barrier counter) moves only through device-scope atomics, loads and
+//    stores, so no L2 write-back or invalidation is ever issued.  The
+//    workspace is left zeroed by every call: the last phase of the kernel
+//    clears the slots and counters for the next call, so a call is a single
+//    launch.
 #include "device_util.h"
 #include "launch.h"
 
@@ -49,7 +55,7 @@ struct DraftParams {
   float* logit;
   float* conf;
   float* surv;
-  unsigned int* ctrl;  // [0] barrier arrivals, [1] error flag
+  unsigned int* ctrl;  // [0] barrier arrivals, [1] error flag, [2] exit arrivals
   uint64_t* slots;     // [gamma][B] packed argmax keys
   float* zpart;        // [2][nwg][B] logit of each workgroup's local winner
   double* hdot;        // [B][gamma] hidden-state part of the confidence logit
@@ -98,7 +104,7 @@ struct RawU<false> {
 
 __device__ __forceinline__ void load_u(RawU<true>& r, const uint16_t* row, int v0, int V, int vec_ok) {
   if (vec_ok) {
-    r.q = (v0 < V) ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(row + v0)) : u32x2_t{0u, 0u};
+    r.q = (v0 < V) ? *reinterpret_cast<const u32x2_t*>(row + v0) : u32x2_t{0u, 0u};
   } else {
     uint32_t e[4];
 #pragma unroll
@@ -108,7 +114,7 @@ __device__ __forceinline__ void load_u(RawU<true>& r, const uint16_t* row, int v
 }
 __device__ __forceinline__ void load_u(RawU<false>& r, const float* row, int v0, int V, int vec_ok) {
   if (vec_ok) {
-    r.q = (v0 < V) ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(row + v0)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    r.q = (v0 < V) ? *reinterpret_cast<const f32x4_t*>(row + v0) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.q[i] = (v0 + i < V) ? row[v0 + i] : 0.f;
@@ -141,44 +147,196 @@ __device__ __forceinline__ int part_of(int t, int n, int parts) {
   return w;
 }
 
-// Loads the base logits of request tile `bt` for this wave's vocabulary
-// tiles: lane (li, lg) gets U[b][k-1][tile*16 + 4*lg .. +3] with
-// b = g0 + 16*bt + li (clamped into the batch; such lanes are ignored).
-template <bool BF16, int TPW>
-__device__ __forceinline__ void load_tile(RawU<BF16> (&buf)[TPW], const typename Elem<BF16>::store_t* U, int g0,
-                                          int bt, int li, int lg, int B, int gamma, int k, int V, int w_lo, int nt,
-                                          int vec_ok) {
-  const int b = min(g0 + bt * 16 + li, B - 1);
-  const typename Elem<BF16>::store_t* urow = U + (size_t(b) * gamma + (k - 1)) * V;
+// Unconditional load of four base logits (full tile inside the vocabulary,
+// V % 4 == 0).  Plain (temporal) loads: the four vocabulary tiles that share
+// a 128-byte line of a row are read by consecutive instructions of the same
+// wave and should hit in L1.
+__device__ __forceinline__ void load_u_full(RawU<true>& r, const uint16_t* p) {
+  r.q = *reinterpret_cast<const u32x2_t*>(p);
+}
+__device__ __forceinline__ void load_u_full(RawU<false>& r, const float* p) {
+  r.q = *reinterpret_cast<const f32x4_t*>(p);
+}
+
+// Phase 4 of a draft step for one wave: for every 16-request tile of the
+// group, z = U_k + e W2 over the wave's NTF vocabulary tiles (accumulator
+// initialised with U_k, MFMA over the rank), then the argmax over z (greedy)
+// or z + Gumbel noise, merged into the workgroup's per-request LDS key.
+//
+// Per lane and request tile the argmax runs tile by tile: the tile maximum,
+// a strict comparison with the running best (so the earliest tile wins
+// ties) that keeps the best tile's index and its four scores, and at the end
+// the first of those four equal to the best score: the lowest vocabulary id
+// among equal maxima.
+//
+// The U loads of request tile bt + 3 are issued right after tile bt's
+// buffer has been widened into the accumulators, into that same buffer
+// (three fixed buffers, no rotation), with the tile index clamped at the end
+// so the issue never sits behind a branch; the B-operand fragment is read
+// one K step ahead.  CHECKED handles a wave with fewer than NTF tiles, a tile
+// crossing the end of the vocabulary and V % 4 != 0; the unchecked form has
+// no per-tile branches.
+template <bool BF16, int R, int TPW, int GR, bool GUMBEL, int NTF, bool CHECKED>
+struct TileWork {
+  typedef Elem<BF16> E;
+  typedef typename E::store_t st_t;
+  typedef typename E::frag_t frag_t;
+  static constexpr int NKS = R / E::KS;
+  static constexpr int LDE = R + E::PAD;
+
+  const frag_t (&A)[TPW][NKS];
+  const st_t* lds_e;
+  const st_t* U;
+  uint64_t* lds_key;
+  float* lds_zw;
+  size_t row_stride;   // gamma * V elements between consecutive requests
+  const st_t* ubase;   // U[g0][k-1][vlane] for this lane's column of the tile
+  int g0, rows, nbt, B, k, V, w_lo, nt, vec_ok, li, lg, vlane;
+  uint32_t seed_lo, seed_hi;
+
+  __device__ __forceinline__ void issue(RawU<BF16> (&bb)[NTF], int bt) const {
+    const int r = min(min(bt, nbt - 1) * 16 + li, rows - 1);   // clamped into the group
+    const st_t* p = ubase + size_t(r) * row_stride;
+    if constexpr (CHECKED) {
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
-    if (t < nt) load_u(buf[t], urow, (w_lo + t) * 16 + 4 * lg, V, vec_ok);
-}
-
-// Zeroes the barrier counter, the error flag and the argmax slots, and
-// precomputes hdot[b][k] = sum_j conf_w[j] h[b][k][j] in fp64 (one wave per
-// (b, k)); this half of the confidence logit does not depend on the tokens.
-template <bool BF16>
-__global__ __launch_bounds__(256) void draft_init_kernel(DraftParams p) {
-  typedef typename Elem<BF16>::store_t st_t;
-  const int gtid = blockIdx.x * 256 + threadIdx.x;
-  const int nthreads = gridDim.x * 256;
-  const long long nslots = (long long)p.gamma * p.B;
-  for (long long i = gtid; i < nslots; i += nthreads) p.slots[i] = 0ull;
-  if (gtid < 2) p.ctrl[gtid] = 0u;
-  const int lane = threadIdx.x & 63;
-  const int nwaves = nthreads >> 6;
-  const st_t* h = static_cast<const st_t*>(p.h);
-  for (int bk = gtid >> 6; bk < p.B * p.gamma; bk += nwaves) {
-    const st_t* row = h + size_t(bk) * p.d;
-    double acc = 0.0;
-    for (int j = lane; j < p.d; j += 64) acc += double(p.conf_w[j]) * double(to_f32(row[j]));
-    acc = wave_sum_f64(acc);
-    if (lane == 0) p.hdot[bk] = acc;
+      for (int t = 0; t < NTF; ++t)
+        if (t < nt) load_u(bb[t], p - vlane, vlane + 16 * t, V, vec_ok);   // row start, column
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTF; ++t) load_u_full(bb[t], p + 16 * min(t, nt - 1));
+    }
   }
+
+  __device__ __forceinline__ void step(RawU<BF16> (&bb)[NTF], int bt) const {
+    f32x4_t acc[NTF];
+#pragma unroll
+    for (int t = 0; t < NTF; ++t) acc[t] = widen_u(bb[t]);
+    issue(bb, bt + 3);
+    const st_t* erow = lds_e + (bt * 16 + li) * LDE + E::KPL * lg;
+    frag_t bfr = lds_frag(erow);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const frag_t cur = bfr;
+      if (ks + 1 < NKS) bfr = lds_frag(erow + (ks + 1) * E::KS);
+#pragma unroll
+      for (int t = 0; t < NTF; ++t) {
+        if constexpr (CHECKED) {
+          if (t < nt) acc[t] = mfma16(A[t][ks], cur, acc[t]);
+        } else {
+          acc[t] = mfma16(A[t][ks], cur, acc[t]);
+        }
+      }
+    }
+    const int brow = bt * 16 + li;
+    const int b = g0 + brow;
+    float bs = -INFINITY;
+    int btile = -1;
+    f32x4_t bsel = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t bzsel = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NTF; ++t) {
+      if (CHECKED && t >= nt) continue;
+      // unchecked: a padded tile (t >= nt) repeats tile nt-1, ids and noise included
+      const int tv = CHECKED ? t : min(t, nt - 1);
+      f32x4_t s4 = acc[t];
+      if constexpr (GUMBEL) {
+        uint32_t c0 = uint32_t(vlane + 16 * tv) >> 2, c1 = uint32_t(k), c2 = uint32_t(b), c3 = 0u;
+        philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
+        s4 += f32x4_t{gumbel_from_word(c0), gumbel_from_word(c1), gumbel_from_word(c2), gumbel_from_word(c3)};
+      }
+      if constexpr (CHECKED) {   // ids past the vocabulary never win
+        const int v0 = vlane + 16 * t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (v0 + i >= V) s4[i] = -INFINITY;
+      }
+      const float mt = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+      if (!CHECKED && t == 0) {   // finite scores: tile 0 always starts the running best
+        bs = mt;
+        btile = 0;
+        bsel = s4;
+        if constexpr (GUMBEL) bzsel = acc[0];
+        continue;
+      }
+      const bool take = mt > bs;
+      bs = take ? mt : bs;
+      btile = take ? tv : btile;
+      bsel = take ? s4 : bsel;
+      if constexpr (GUMBEL) bzsel = take ? acc[t] : bzsel;
+    }
+    int bi = (bsel[2] == bs) ? 2 : 3;
+    bi = (bsel[1] == bs) ? 1 : bi;
+    bi = (bsel[0] == bs) ? 0 : bi;
+    uint64_t key = (btile < 0) ? 0ull : argmax_key(bs, uint32_t(vlane + 16 * btile + bi));
+    if constexpr (!GUMBEL) {
+      // every lane merges its own candidate: no cross-lane round trip
+      if (b < B && key != 0ull)
+        __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(&lds_key[brow]), (unsigned long long)key,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      // the winner's unperturbed logit travels with the key
+      float bz = (bi == 0) ? bzsel[0] : (bi == 1) ? bzsel[1] : (bi == 2) ? bzsel[2] : bzsel[3];
+#pragma unroll
+      for (int m = 16; m <= 32; m <<= 1) {
+        const uint64_t ok = shfl_xor_u64(key, m);
+        const float oz = __shfl_xor(bz, m, 64);
+        if (ok > key) bz = oz;
+        key = ok > key ? ok : key;
+      }
+      if (lg == 0 && b < B && key != 0ull) {
+        __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(&lds_key[brow]), (unsigned long long)key,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        lds_zw[brow] = bz;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void run() const {
+    RawU<BF16> b0[NTF], b1[NTF], b2[NTF];
+    issue(b0, 0);
+    issue(b1, 1);
+    issue(b2, 2);
+    // Straight-line loop body (the compiler's wait counts stay exact across
+    // the back edge: consuming a buffer waits only for its own five loads);
+    // the last one or two request tiles run after the loop.
+    int bt = 0;
+    for (; bt + 3 <= nbt; bt += 3) {
+      step(b0, bt);
+      step(b1, bt + 1);
+      step(b2, bt + 2);
+    }
+    if (bt < nbt) step(b0, bt);
+    if (bt + 1 < nbt) step(b1, bt + 1);
+  }
+};
+
+template <bool BF16, int R, int TPW, int GR, bool GUMBEL, int NTF, bool CHECKED>
+__device__ __forceinline__ void compute_tiles(const typename Elem<BF16>::frag_t (&A)[TPW][R / Elem<BF16>::KS],
+                                              const typename Elem<BF16>::store_t* lds_e,
+                                              const typename Elem<BF16>::store_t* U, int g0, int rows, int B,
+                                              int gamma, int k, int V, int w_lo, int nt, int vec_ok, int li, int lg,
+                                              uint32_t seed_lo, uint32_t seed_hi, uint64_t* lds_key, float* lds_zw) {
+  const int vlane = w_lo * 16 + 4 * lg;
+  const size_t row_stride = size_t(gamma) * V;
+  TileWork<BF16, R, TPW, GR, GUMBEL, NTF, CHECKED> w{
+      A, lds_e, U, lds_key, lds_zw, row_stride, U + (size_t(g0) * gamma + (k - 1)) * V + vlane,
+      g0, rows, (rows + 15) >> 4, B, k, V, w_lo, nt, vec_ok, li, lg, vlane, seed_lo, seed_hi};
+  w.run();
 }
 
-template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL>
+// Hidden-state half of the confidence logit, hdot[b][k] = sum_j conf_w[j] *
+// h[b][k][j], accumulated in fp64 by one wave (it does not depend on the
+// drafted tokens).
+template <typename st_t>
+__device__ __forceinline__ double hidden_dot(const st_t* row, const float* w, int d, int lane) {
+  double acc = 0.0;
+  for (int j = lane; j < d; j += 64) acc += double(w[j]) * double(to_f32(row[j]));
+  return wave_sum_f64(acc);
+}
+
+// FULL: V % 16 == 0, every vocabulary tile is whole and rows are 8-byte
+// aligned, so the branch-free tile path is used; otherwise the guarded path.
+template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL>
 __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p) {
   typedef Elem<BF16> E;
   typedef typename E::store_t st_t;
@@ -198,6 +356,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   __shared__ int lds_x[GR];
   __shared__ double lds_hd[GR];
   __shared__ float lds_S[kMaxOwnedRows];
+  __shared__ float lds_we[R];   // confidence weights of the Markov-embedding half
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -211,6 +370,22 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   const int wg_nt = part_start(wg + 1, p.tiles, nwg) - wg_lo;
   const int w_lo = wg_lo + part_start(wave, wg_nt, NW);
   const int nt = wg_lo + part_start(wave + 1, wg_nt, NW) - w_lo;   // <= TPW
+
+  // A workspace left by a completed call has a zero barrier counter; before
+  // this workgroup's first arrival at most nwg - 1 others can have arrived.
+  if (tid == 0 && load_dev(&p.ctrl[0]) >= unsigned(nwg)) store_dev(&p.ctrl[1], 2u);
+
+  // hdot for every (owned request, position): one (b, k) per wave at a time.
+  {
+    const st_t* h = static_cast<const st_t*>(p.h);
+    const int nown = (B > wg) ? (B - 1 - wg) / nwg + 1 : 0;
+    for (int q = wave; q < nown * gamma; q += NW) {
+      const int b = wg + (q / gamma) * nwg, kk = q % gamma;
+      const double v = hidden_dot(h + (size_t(b) * gamma + kk) * p.d, p.conf_w, p.d, lane);
+      if (lane == 0) store_dev(&p.hdot[size_t(b) * gamma + kk], v);
+    }
+    wait_vmem();   // visible to the other waves after the next workgroup barrier
+  }
 
   // W2 slice of this wave in MFMA A-operand layout, resident for the call.
   // The workgroup's columns [wg_lo*16, wg_hi*16) of W2 are staged through
@@ -235,8 +410,8 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       __syncthreads();
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        if (t < nt) {   // columns of tile t lie inside the staged slice
-          const int c = (w_lo - wg_lo + t) * 16 + li;
+        if (nt > 0) {   // tiles past the wave's range repeat its last tile
+          const int c = (w_lo - wg_lo + min(t, nt - 1)) * 16 + li;
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const int kr = ks * E::KS + E::KPL * lg - kc;   // kn is a multiple of KS: kr..kr+KPL-1 all staged
@@ -258,6 +433,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     }
   }
   for (int i = tid; i < kMaxOwnedRows; i += NT) lds_S[i] = 1.0f;
+  for (int i = tid; i < R; i += NT) lds_we[i] = p.conf_w[p.d + i];
   for (int i = tid; i < GR; i += NT) lds_key[i] = 0ull;
 
   const st_t* U = static_cast<const st_t*>(p.U);
@@ -300,7 +476,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           }
         }
         lds_x[tid] = x;
-        if (own) lds_hd[tid] = p.hdot[size_t(b) * gamma + (k - 1)];
+        if (own) lds_hd[tid] = load_dev(&p.hdot[size_t(b) * gamma + (k - 1)]);
       }
       __syncthreads();
 
@@ -314,7 +490,25 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       }
       __syncthreads();
 
-      // 3. confidence + STS + survival for the rows this workgroup owns
+      // 4. z = U_k + e W2 on MFMA, argmax in registers, per request tile
+      {
+        // Whole tiles: branch-free path over exactly TPW tiles (a wave with
+        // fewer tiles repeats its last one, whose equal scores at the same ids
+        // never win the strict comparison).
+        if (nt > 0) {
+          if constexpr (FULL)
+            compute_tiles<BF16, R, TPW, GR, GUMBEL, TPW, false>(A, lds_e, U, g0, rows, B, gamma, k, V, w_lo, nt,
+                                                                p.vec_ok, li, lg, p.seed_lo, p.seed_hi, lds_key,
+                                                                lds_z[wave]);
+          else
+            compute_tiles<BF16, R, TPW, GR, GUMBEL, TPW, true>(A, lds_e, U, g0, rows, B, gamma, k, V, w_lo, nt,
+                                                               p.vec_ok, li, lg, p.seed_lo, p.seed_hi, lds_key,
+                                                               lds_z[wave]);
+        }
+      }
+
+      // 3. confidence + STS + survival for the rows this workgroup owns (after the
+      //    MFMA phase: it only needs e, which stays in LDS until the next gather)
       {
         const int j_lo = (g0 > wg) ? (g0 - wg + nwg - 1) / nwg : 0;
         const int j_hi = (g0 + rows > wg) ? (g0 + rows - wg + nwg - 1) / nwg : 0;
@@ -322,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           const int b = wg + j * nwg;
           const int row = b - g0;
           double acc = 0.0;
-          for (int i = lane; i < R; i += 64) acc += double(p.conf_w[p.d + i]) * double(to_f32(lds_e[row * LDE + i]));
+          for (int i = lane; i < R; i += 64) acc += double(lds_we[i]) * double(to_f32(lds_e[row * LDE + i]));
           acc = wave_sum_f64(acc);
           if (lane == 0) {
             const double ell = double(p.conf_b) + (lds_hd[row] + acc);
@@ -336,63 +530,6 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
         }
       }
 
-      // 4. z = U_k + e W2 on MFMA, argmax in registers, per request tile
-      const int nbt = (rows + 15) >> 4;
-      RawU<BF16> ubuf[TPW];
-      load_tile<BF16, TPW>(ubuf, U, g0, 0, li, lg, B, gamma, k, V, w_lo, nt, p.vec_ok);
-      for (int bt = 0; bt < nbt; ++bt) {
-        f32x4_t acc[TPW];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t] = widen_u(ubuf[t]);
-        if (bt + 1 < nbt) load_tile<BF16, TPW>(ubuf, U, g0, bt + 1, li, lg, B, gamma, k, V, w_lo, nt, p.vec_ok);
-        const st_t* erow = lds_e + (bt * 16 + li) * LDE + E::KPL * lg;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const frag_t bfr = lds_frag(erow + ks * E::KS);
-#pragma unroll
-          for (int t = 0; t < TPW; ++t)
-            if (t < nt) acc[t] = mfma16(A[t][ks], bfr, acc[t]);
-        }
-        const int brow = bt * 16 + li;
-        const int b = g0 + brow;
-        float bs = -INFINITY, bz = 0.f;
-        uint32_t bv = 0xFFFFFFFFu;
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-          if (t < nt) {
-            const int v0 = (w_lo + t) * 16 + 4 * lg;
-            f32x4_t s4 = acc[t];
-            if constexpr (GUMBEL) {
-              uint32_t c0 = uint32_t(v0) >> 2, c1 = uint32_t(k), c2 = uint32_t(b), c3 = 0u;
-              philox4x32_10(c0, c1, c2, c3, p.seed_lo, p.seed_hi);
-              s4 += f32x4_t{gumbel_from_word(c0), gumbel_from_word(c1), gumbel_from_word(c2),
-                            gumbel_from_word(c3)};
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (v0 + i < V && s4[i] > bs) {
-                bs = s4[i];
-                bv = uint32_t(v0 + i);
-                bz = acc[t][i];
-              }
-            }
-          }
-        }
-        uint64_t key = (bv == 0xFFFFFFFFu) ? 0ull : argmax_key(bs, bv);
-#pragma unroll
-        for (int m = 16; m <= 32; m <<= 1) {
-          const uint64_t ok = shfl_xor_u64(key, m);
-          const float oz = __shfl_xor(bz, m, 64);
-          if (ok > key) {
-            key = ok;
-            bz = oz;
-          }
-        }
-        if (lg == 0 && b < B && key != 0ull) {
-          atomicMax(reinterpret_cast<unsigned long long*>(&lds_key[brow]), (unsigned long long)key);
-          lds_z[wave][brow] = bz;
-        }
-      }
       __syncthreads();
 
       // 5. publish this workgroup's winner of every row of the group
@@ -405,18 +542,40 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
                                  (unsigned long long)key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const int tile = int(key_index(key) >> 4);
           const int w = part_of(tile - wg_lo, wg_nt, NW);
-          p.zpart[(size_t((k & 1) * nwg + wg)) * B + b] = lds_z[w][tid];
+          store_dev(&p.zpart[(size_t((k & 1) * nwg + wg)) * B + b], GUMBEL ? lds_z[w][tid] : key_value(key));
         }
       }
       __syncthreads();
     }
     grid_barrier(&p.ctrl[0], &p.ctrl[1], unsigned(k) * unsigned(nwg), p.spin_limit);
   }
-  // outputs of the last step
+  // outputs of the last step; a failed synchronisation marks every token -1
+  const bool failed = load_dev(&p.ctrl[1]) != 0u;
   for (int b = wg + tid * nwg; b < B; b += NT * nwg) {
-    const uint64_t key = __hip_atomic_load(&p.slots[size_t(gamma - 1) * B + b], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t key = load_dev(&p.slots[size_t(gamma - 1) * B + b]);
     emit(b, gamma, key);
+    if (failed)
+      for (int kk = 0; kk < gamma; ++kk) p.tokens[size_t(b) * gamma + kk] = -1;
+  }
+
+  // Leave the workspace as a fresh call expects it: once every workgroup is
+  // done reading, workgroup 0 clears the argmax slots and the counters.
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) __hip_atomic_fetch_add(&p.ctrl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wg == 0) {
+    if (tid == 0) {
+      unsigned int polls = 0;
+      while (load_dev(&p.ctrl[2]) < unsigned(nwg) && ++polls <= p.spin_limit) __builtin_amdgcn_s_sleep(1);
+    }
+    __syncthreads();
+    const long long nslots = (long long)gamma * B;
+    for (long long i = tid; i < nslots; i += NT) store_dev(&p.slots[i], uint64_t(0));
+    if (tid == 0) {
+      store_dev(&p.ctrl[0], 0u);
+      store_dev(&p.ctrl[1], 0u);
+      store_dev(&p.ctrl[2], 0u);
+    }
   }
 }
 
@@ -427,27 +586,33 @@ struct KernelChoice {
 };
 
 template <bool BF16, int R, bool G>
-KernelChoice pick_r() {
+KernelChoice pick_r(bool full) {
   constexpr int NW = 8, GR = 256;
   constexpr int TPW = BF16 ? 5 : 4;
-  return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G>), NW * 64, TPW};
+  if constexpr (BF16) {
+    if (full)
+      return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, true>),
+                          NW * 64, TPW};
+  }
+  return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, false>), NW * 64,
+                      TPW};
 }
 
 template <bool G>
-bool pick(bool bf16, int r, KernelChoice* out) {
+bool pick(bool bf16, int r, bool full, KernelChoice* out) {
   if (bf16) {
     switch (r) {
-      case 32: *out = pick_r<true, 32, G>(); return true;
-      case 64: *out = pick_r<true, 64, G>(); return true;
-      case 128: *out = pick_r<true, 128, G>(); return true;
-      case 256: *out = pick_r<true, 256, G>(); return true;
+      case 32: *out = pick_r<true, 32, G>(full); return true;
+      case 64: *out = pick_r<true, 64, G>(full); return true;
+      case 128: *out = pick_r<true, 128, G>(full); return true;
+      case 256: *out = pick_r<true, 256, G>(full); return true;
       default: return false;
     }
   }
   switch (r) {
-    case 16: *out = pick_r<false, 16, G>(); return true;
-    case 32: *out = pick_r<false, 32, G>(); return true;
-    case 64: *out = pick_r<false, 64, G>(); return true;
+    case 16: *out = pick_r<false, 16, G>(full); return true;
+    case 32: *out = pick_r<false, 32, G>(full); return true;
+    case 64: *out = pick_r<false, 64, G>(full); return true;
     default: return false;
   }
 }
@@ -495,7 +660,8 @@ DraftWorkspace draft_workspace_layout(int B, int gamma) {
 hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported) {
   *unsupported = nullptr;
   KernelChoice kc;
-  const bool ok = a.gumbel ? pick<true>(a.bf16, a.r, &kc) : pick<false>(a.bf16, a.r, &kc);
+  const bool full = (a.V % 16) == 0;
+  const bool ok = a.gumbel ? pick<true>(a.bf16, a.r, full, &kc) : pick<false>(a.bf16, a.r, full, &kc);
   if (!ok) {
     *unsupported = a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
                           : "fp32 drafting supports r in {16, 32, 64}";
@@ -548,15 +714,6 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   p.zpart = reinterpret_cast<float*>(ws + L.zpart);
   p.hdot = reinterpret_cast<double*>(ws + L.hdot);
 
-  int init_blocks = (a.B * a.gamma + 3) / 4;
-  if (init_blocks > 1024) init_blocks = 1024;
-  if (init_blocks < 1) init_blocks = 1;
-  if (a.bf16)
-    hipLaunchKernelGGL(draft_init_kernel<true>, dim3(init_blocks), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(draft_init_kernel<false>, dim3(init_blocks), dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   void* args[] = {&p};
   return hipLaunchCooperativeKernel(kc.fn, dim3(nwg), dim3(kc.threads), args, 0, stream);
 }

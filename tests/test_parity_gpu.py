@@ -234,3 +234,21 @@ def test_chained_gumbel_iterations():
         d, out = run_case(w)
         lens, acc, bonus = end_to_end(w, d, out)
         anchor = bonus
+
+
+def test_dirty_workspace_is_flagged_and_cleaned():
+    """A workspace that was not zero-filled is detected (all tokens -1) and the
+    call leaves it clean, so the next call is correct."""
+    from semi_ar_drafter_amd import binding, markov_draft
+    w = wl.make_workload(wl.small_config(B=20, gamma=3, V=2000, r=32, d=16, dtype="bf16"))
+    d = to_device(w)
+    nb = binding.workspace_bytes(20, 3, 2000, 32)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    args = (d["anchor"], d["U"], d["h"], d["W1"], d["W2"], d["conf_w"], d["conf_b"], d["sts_T"])
+    tok, _, _, _ = markov_draft(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert (tok.cpu().numpy() == -1).all()
+    out = markov_draft(*args, workspace=ws)
+    torch.cuda.synchronize()
+    st = check_draft(w, tuple(x.cpu().numpy() for x in out))
+    assert st.ok(), st
