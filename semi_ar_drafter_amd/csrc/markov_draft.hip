@@ -326,11 +326,48 @@ __device__ __forceinline__ void compute_tiles(const typename Elem<BF16>::frag_t 
 
 // Hidden-state half of the confidence logit, hdot[b][k] = sum_j conf_w[j] *
 // h[b][k][j], accumulated in fp64 by one wave (it does not depend on the
-// drafted tokens).
-template <typename st_t>
-__device__ __forceinline__ double hidden_dot(const st_t* row, const float* w, int d, int lane) {
+// drafted tokens).  bf16 rows with d % 8 == 0 are read 16 bytes per lane,
+// four chunks in flight at a time.
+__device__ __forceinline__ double hidden_dot(const uint16_t* row, const float* w, int d, int lane) {
   double acc = 0.0;
-  for (int j = lane; j < d; j += 64) acc += double(w[j]) * double(to_f32(row[j]));
+  if ((d & 7) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+    const u32x4_t* r16 = reinterpret_cast<const u32x4_t*>(row);
+    const f32x4_t* w16 = reinterpret_cast<const f32x4_t*>(w);
+    const int nch = d >> 3;
+    int c = lane;
+    for (; c + 192 < nch; c += 256) {
+      u32x4_t q[4];
+      f32x4_t wa[4], wb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        q[u] = r16[c + 64 * u];
+        wa[u] = w16[2 * (c + 64 * u)];
+        wb[u] = w16[2 * (c + 64 * u) + 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc += double(wa[u][0]) * double(bf16_lo(q[u][0])) + double(wa[u][1]) * double(bf16_hi(q[u][0]));
+        acc += double(wa[u][2]) * double(bf16_lo(q[u][1])) + double(wa[u][3]) * double(bf16_hi(q[u][1]));
+        acc += double(wb[u][0]) * double(bf16_lo(q[u][2])) + double(wb[u][1]) * double(bf16_hi(q[u][2]));
+        acc += double(wb[u][2]) * double(bf16_lo(q[u][3])) + double(wb[u][3]) * double(bf16_hi(q[u][3]));
+      }
+    }
+    for (; c < nch; c += 64) {
+      const u32x4_t q = r16[c];
+      const f32x4_t wa = w16[2 * c], wb = w16[2 * c + 1];
+      acc += double(wa[0]) * double(bf16_lo(q[0])) + double(wa[1]) * double(bf16_hi(q[0]));
+      acc += double(wa[2]) * double(bf16_lo(q[1])) + double(wa[3]) * double(bf16_hi(q[1]));
+      acc += double(wb[0]) * double(bf16_lo(q[2])) + double(wb[1]) * double(bf16_hi(q[2]));
+      acc += double(wb[2]) * double(bf16_lo(q[3])) + double(wb[3]) * double(bf16_hi(q[3]));
+    }
+  } else {
+    for (int j = lane; j < d; j += 64) acc += double(w[j]) * double(bf16_to_f32(row[j]));
+  }
+  return wave_sum_f64(acc);
+}
+__device__ __forceinline__ double hidden_dot(const float* row, const float* w, int d, int lane) {
+  double acc = 0.0;
+  for (int j = lane; j < d; j += 64) acc += double(w[j]) * double(row[j]);
   return wave_sum_f64(acc);
 }
 
@@ -348,7 +385,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   static_assert(R % E::KS == 0, "rank must be a multiple of the MFMA K step");
 
   constexpr int CMAX = TPW * NW * 16;                       // widest column slice of a workgroup
-  constexpr int SLD = CMAX + (BF16 ? 2 : 1);                // W2 staging row stride (elements)
+  constexpr int SLD = CMAX + (BF16 ? 8 : 4);                // W2 staging row stride (16-byte multiple)
   constexpr int EBUF = (GR * LDE > E::KS * SLD) ? GR * LDE : E::KS * SLD;
   __shared__ __attribute__((aligned(16))) st_t lds_e[EBUF];
   __shared__ uint64_t lds_key[GR];
@@ -402,10 +439,36 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     const int ncols = wg_nt * 16;
     for (int kc = 0; kc < R; kc += KCH) {
       const int kn = min(KCH, R - kc);
-      for (int i = tid; i < kn * ncols; i += NT) {
-        const int kr = i / ncols, c = i - kr * ncols;
-        const int v = col0 + c;
-        stage[kr * SLD + c] = (v < V) ? W2[size_t(kc + kr) * V + v] : st_t(0);
+      constexpr int EPC = 16 / int(sizeof(st_t));             // elements per 16-byte chunk
+      if (FULL && (V % EPC) == 0) {
+        // whole tiles, 16-byte aligned rows: 16-byte loads, eight in flight
+        const int cpr = ncols / EPC;                         // chunks per staged row
+        const int nch = kn * cpr;
+        for (int i0 = tid; i0 < nch; i0 += 8 * NT) {
+          u32x4_t q[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * NT;
+            if (i < nch) {
+              const int kr = i / cpr, c = i - kr * cpr;
+              q[u] = *reinterpret_cast<const u32x4_t*>(W2 + size_t(kc + kr) * V + col0 + c * EPC);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * NT;
+            if (i < nch) {
+              const int kr = i / cpr, c = i - kr * cpr;
+              *reinterpret_cast<u32x4_t*>(stage + kr * SLD + c * EPC) = q[u];
+            }
+          }
+        }
+      } else {
+        for (int i = tid; i < kn * ncols; i += NT) {
+          const int kr = i / ncols, c = i - kr * ncols;
+          const int v = col0 + c;
+          stage[kr * SLD + c] = (v < V) ? W2[size_t(kc + kr) * V + v] : st_t(0);
+        }
       }
       __syncthreads();
 #pragma unroll
@@ -481,12 +544,24 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       __syncthreads();
 
       // 2. gather e = W1[x_{k-1}] for the group's rows into LDS
-      for (int c = tid; c < GR * CHUNKS; c += NT) {
-        const int row = c / CHUNKS, ch = c - row * CHUNKS;
-        u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < rows)
-          val = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(W1 + size_t(lds_x[row]) * R) + ch * 16);
-        *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(lds_e + row * LDE) + ch * 16) = val;
+      // (eight 16-byte loads in flight per thread before their LDS stores)
+      for (int c0 = tid; c0 < GR * CHUNKS; c0 += 8 * NT) {
+        u32x4_t val[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * NT;
+          const int row = c / CHUNKS, ch = c - row * CHUNKS;
+          val[u] = u32x4_t{0u, 0u, 0u, 0u};
+          if (c < GR * CHUNKS && row < rows)
+            val[u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(W1 + size_t(lds_x[row]) * R) +
+                                                       ch * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * NT;
+          const int row = c / CHUNKS, ch = c - row * CHUNKS;
+          if (c < GR * CHUNKS) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(lds_e + row * LDE) + ch * 16) = val[u];
+        }
       }
       __syncthreads();
 
