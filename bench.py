@@ -28,6 +28,49 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+DRAFT_SOURCE = os.path.join(ROOT, "semi_ar_drafter_amd", "csrc", "markov_draft.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "markov_draft_hbm_traffic.txt")
+
+
+def source_digest(path: str) -> str:
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per draft launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the factor a plain copy
+    kernel of known size gives), or None if the summary is missing or was
+    taken on a different version of the draft kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    try:
+        if vals.get("kernel_source_sha256") != source_digest(DRAFT_SOURCE):
+            return None
+        fetch = float(vals["fetch_kib_per_launch"]) * 1024 * float(vals["fetch_scale"])
+        write = float(vals["write_kib_per_launch"]) * 1024 * float(vals["write_scale"])
+        return int(round(fetch + write))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    counters (each launch reads and writes `nbytes`)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def algorithmic_bytes(cfg) -> int:
@@ -45,10 +88,10 @@ def flops(cfg) -> int:
     return 2 * cfg.B * cfg.gamma * cfg.r * cfg.V
 
 
-def cpu_baseline(w, rows: int):
+def cpu_baseline(w, rows: int, min_seconds: float):
     """The oracle as it stands, drafting the first `rows` requests through all
-    gamma steps (requests are independent, so this is a fixed fraction of
-    the call's work)."""
+    gamma steps (requests are independent, so the sample is a fixed fraction
+    of the call's work), repeated until at least `min_seconds` have passed."""
     import numpy as np
     from oracle import dspark_oracle as orc
     try:
@@ -56,10 +99,15 @@ def cpu_baseline(w, rows: int):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    reps = 0
     t0 = time.perf_counter()
-    tok, logit, conf, surv = orc.draft_workload(w, rows=np.arange(rows))
+    while True:
+        orc.draft_workload(w, rows=np.arange(rows))
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     t1 = time.perf_counter()
-    return dict(seconds=t1 - t0, tokens=rows * w["cfg"].gamma, threads=threads)
+    return dict(seconds=t1 - t0, tokens=reps * rows * w["cfg"].gamma, threads=threads, reps=reps)
 
 
 def main():
@@ -68,8 +116,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload id (default: the B=256 configuration)")
-    ap.add_argument("--cpu-rows", type=int, default=64, help="requests in the CPU-oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="requests in the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (for HBM counter scaling) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -87,6 +138,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        copy_calibration(args.calibrate_copy, 5)
+        return
     cfg = wl.CONFIGS[args.config]
     t_gen = time.perf_counter()
     w = wl.make_workload(cfg)
@@ -162,19 +216,21 @@ def main():
                    "d": cfg.d, "storage": cfg.dtype, "sampling": cfg.sampling,
                    "sps_table": "64-point 4+0.02n+2e-5n^2, n in [256, 4352]"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "markov_draft (per dspark_markov_draft call)",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
+                     "kernel": "markov_draft_kernel (one launch per dspark_markov_draft call)",
                      "algorithmic_bytes_per_launch": abytes, "launch_us": round(draft_avg * 1e3, 2)},
         "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(w, args.cpu_rows)
+        cb = cpu_baseline(w, min(args.cpu_rows, B), args.cpu_seconds)
         result["cpu_baseline"] = {"value": round(cb["tokens"] / cb["seconds"], 2), "unit": "drafted tokens/s",
                                   "cores": cb["threads"], "kind": "oracle",
-                                  "sample": f"first {args.cpu_rows} of {B} requests, all {g} draft steps "
-                                            f"({cb['seconds']:.1f}s, host has {os.cpu_count()} CPUs)"}
+                                  "sample": f"{cb['reps']} x first {min(args.cpu_rows, B)} of {B} requests, all "
+                                            f"{g} draft steps ({cb['seconds']:.1f}s; host reports "
+                                            f"{os.cpu_count()} CPUs)"}
     print(json.dumps(result), flush=True)
 
 
