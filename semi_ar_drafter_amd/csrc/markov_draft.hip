@@ -35,6 +35,8 @@
 #include "device_util.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace dspark {
 namespace {
 
@@ -147,15 +149,25 @@ __device__ __forceinline__ int part_of(int t, int n, int parts) {
   return w;
 }
 
-// Unconditional load of four base logits (full tile inside the vocabulary,
-// V % 4 == 0).  Plain (temporal) loads: the four vocabulary tiles that share
-// a 128-byte line of a row are read by consecutive instructions of the same
-// wave and should hit in L1.
-__device__ __forceinline__ void load_u_full(RawU<true>& r, const uint16_t* p) {
-  r.q = *reinterpret_cast<const u32x2_t*>(p);
-}
-__device__ __forceinline__ void load_u_full(RawU<false>& r, const float* p) {
-  r.q = *reinterpret_cast<const f32x4_t*>(p);
+// Column layout of the branch-free path.  Tiles are taken in pairs; lane
+// group q of a pair holds 8 consecutive vocabulary ids, 4 in each tile of the
+// pair, so a single 16-byte load per lane fetches the base logits of both
+// tiles (16 requests x 64 contiguous bytes per load instruction instead of
+// 16 x 32).  With TPW odd the last slot is an ordinary 16-wide tile.  A wave
+// owning nt < TPW tiles (nt >= 2) fills its spare slots with exact copies of
+// columns it already holds: a spare pair slot repeats pair 0, a spare last
+// slot repeats the second half of the last real pair.  Returns the first of
+// the four consecutive columns (relative to the wave's first column) that lane
+// group q holds in tile slot t.  Along t the ids a lane sees never decrease
+// except for exact repeats, so a strict comparison in t order still picks the
+// lowest id among equal scores.
+__device__ __forceinline__ int pair_col(int t, int q, int nt, int tpw) {
+  const int rp = nt >> 1;   // complete pairs the wave owns
+  if (t < (tpw & ~1)) {
+    const int pr = t >> 1;
+    return (pr < rp ? 32 * pr : 0) + 8 * q + 4 * (t & 1);
+  }
+  return (nt & 1) ? 32 * rp + 4 * q : 32 * (rp - 1) + 8 * q + 4;
 }
 
 // Phase 4 of a draft step for one wave: for every 16-request tile of the
@@ -173,9 +185,10 @@ __device__ __forceinline__ void load_u_full(RawU<false>& r, const float* p) {
 // buffer has been widened into the accumulators, into that same buffer
 // (three fixed buffers, no rotation), with the tile index clamped at the end
 // so the issue never sits behind a branch; the B-operand fragment is read
-// one K step ahead.  CHECKED handles a wave with fewer than NTF tiles, a tile
-// crossing the end of the vocabulary and V % 4 != 0; the unchecked form has
-// no per-tile branches.
+// one K step ahead.  CHECKED (natural 16-wide tiles) handles a wave with
+// fewer than NTF tiles, a tile crossing the end of the vocabulary and V % 4
+// != 0; the unchecked form (bf16, whole tiles, the pair layout above) has no
+// per-tile branches.
 template <bool BF16, int R, int TPW, int GR, bool GUMBEL, int NTF, bool CHECKED>
 struct TileWork {
   typedef Elem<BF16> E;
@@ -183,34 +196,73 @@ struct TileWork {
   typedef typename E::frag_t frag_t;
   static constexpr int NKS = R / E::KS;
   static constexpr int LDE = R + E::PAD;
+  static constexpr int NP = TPW / 2;               // tile pairs (unchecked form)
+  static constexpr bool LONE = (TPW & 1) != 0;     // unpaired last slot
+  static_assert(CHECKED || (BF16 && NTF == TPW), "the pair layout is for bf16 whole tiles");
+
+  struct CheckedBuf {
+    RawU<BF16> t[NTF];
+  };
+  struct PairBuf {
+    u32x4_t p[NP > 0 ? NP : 1];
+    u32x2_t l;
+  };
+  typedef typename std::conditional<CHECKED, CheckedBuf, PairBuf>::type Buf;
 
   const frag_t (&A)[TPW][NKS];
   const st_t* lds_e;
-  const st_t* U;
   uint64_t* lds_key;
   float* lds_zw;
   size_t row_stride;   // gamma * V elements between consecutive requests
-  const st_t* ubase;   // U[g0][k-1][vlane] for this lane's column of the tile
-  int g0, rows, nbt, B, k, V, w_lo, nt, vec_ok, li, lg, vlane;
+  const st_t* ubase;   // CHECKED: U[g0][k-1][vlane]; else U[g0][k-1][wave's first column]
+  int g0, rows, nbt, B, k, V, nt, vec_ok, li, lg;
+  int vlane;           // CHECKED: first id of this lane's 4 in tile 0; else the wave's first column
+  int oP0, oP1, oL;    // unchecked: columns (relative) of this lane's pair-0 / pair-1 / last-slot loads
   uint32_t seed_lo, seed_hi;
 
-  __device__ __forceinline__ void issue(RawU<BF16> (&bb)[NTF], int bt) const {
+  // first of this lane's four consecutive ids in tile slot t
+  __device__ __forceinline__ int tile_id0(int t) const {
+    if constexpr (CHECKED) {
+      return vlane + 16 * t;
+    } else {
+      if (t < 2 * NP) return vlane + ((t >> 1) == 0 ? oP0 : oP1) + 4 * (t & 1);
+      return vlane + oL;
+    }
+  }
+
+  __device__ __forceinline__ void issue(Buf& bb, int bt) const {
     const int r = min(min(bt, nbt - 1) * 16 + li, rows - 1);   // clamped into the group
     const st_t* p = ubase + size_t(r) * row_stride;
     if constexpr (CHECKED) {
 #pragma unroll
       for (int t = 0; t < NTF; ++t)
-        if (t < nt) load_u(bb[t], p - vlane, vlane + 16 * t, V, vec_ok);   // row start, column
+        if (t < nt) load_u(bb.t[t], p - vlane, vlane + 16 * t, V, vec_ok);   // row start, column
     } else {
-#pragma unroll
-      for (int t = 0; t < NTF; ++t) load_u_full(bb[t], p + 16 * min(t, nt - 1));
+      const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+      static_assert(NP <= 2, "pair offsets kept for two pairs");
+      if constexpr (NP >= 1) bb.p[0] = *reinterpret_cast<const u32x4_t*>(q + oP0);
+      if constexpr (NP >= 2) bb.p[1] = *reinterpret_cast<const u32x4_t*>(q + oP1);
+      if constexpr (LONE) bb.l = *reinterpret_cast<const u32x2_t*>(q + oL);
     }
   }
 
-  __device__ __forceinline__ void step(RawU<BF16> (&bb)[NTF], int bt) const {
-    f32x4_t acc[NTF];
+  __device__ __forceinline__ void widen(const Buf& bb, f32x4_t (&acc)[NTF]) const {
+    if constexpr (CHECKED) {
 #pragma unroll
-    for (int t = 0; t < NTF; ++t) acc[t] = widen_u(bb[t]);
+      for (int t = 0; t < NTF; ++t) acc[t] = widen_u(bb.t[t]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        acc[2 * j] = f32x4_t{bf16_lo(bb.p[j].x), bf16_hi(bb.p[j].x), bf16_lo(bb.p[j].y), bf16_hi(bb.p[j].y)};
+        acc[2 * j + 1] = f32x4_t{bf16_lo(bb.p[j].z), bf16_hi(bb.p[j].z), bf16_lo(bb.p[j].w), bf16_hi(bb.p[j].w)};
+      }
+      if constexpr (LONE) acc[TPW - 1] = f32x4_t{bf16_lo(bb.l.x), bf16_hi(bb.l.x), bf16_lo(bb.l.y), bf16_hi(bb.l.y)};
+    }
+  }
+
+  __device__ __forceinline__ void step(Buf& bb, int bt) const {
+    f32x4_t acc[NTF];
+    widen(bb, acc);
     issue(bb, bt + 3);
     const st_t* erow = lds_e + (bt * 16 + li) * LDE + E::KPL * lg;
     frag_t bfr = lds_frag(erow);
@@ -236,16 +288,14 @@ struct TileWork {
 #pragma unroll
     for (int t = 0; t < NTF; ++t) {
       if (CHECKED && t >= nt) continue;
-      // unchecked: a padded tile (t >= nt) repeats tile nt-1, ids and noise included
-      const int tv = CHECKED ? t : min(t, nt - 1);
       f32x4_t s4 = acc[t];
       if constexpr (GUMBEL) {
-        uint32_t c0 = uint32_t(vlane + 16 * tv) >> 2, c1 = uint32_t(k), c2 = uint32_t(b), c3 = 0u;
+        uint32_t c0 = uint32_t(tile_id0(t)) >> 2, c1 = uint32_t(k), c2 = uint32_t(b), c3 = 0u;
         philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
         s4 += f32x4_t{gumbel_from_word(c0), gumbel_from_word(c1), gumbel_from_word(c2), gumbel_from_word(c3)};
       }
       if constexpr (CHECKED) {   // ids past the vocabulary never win
-        const int v0 = vlane + 16 * t;
+        const int v0 = tile_id0(t);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (v0 + i >= V) s4[i] = -INFINITY;
@@ -260,14 +310,21 @@ struct TileWork {
       }
       const bool take = mt > bs;
       bs = take ? mt : bs;
-      btile = take ? tv : btile;
+      btile = take ? t : btile;
       bsel = take ? s4 : bsel;
       if constexpr (GUMBEL) bzsel = take ? acc[t] : bzsel;
     }
     int bi = (bsel[2] == bs) ? 2 : 3;
     bi = (bsel[1] == bs) ? 1 : bi;
     bi = (bsel[0] == bs) ? 0 : bi;
-    uint64_t key = (btile < 0) ? 0ull : argmax_key(bs, uint32_t(vlane + 16 * btile + bi));
+    int id0;
+    if constexpr (CHECKED) {
+      id0 = vlane + 16 * btile;
+    } else {
+      id0 = (btile >= 2 * NP) ? oL : ((btile >= 2) ? oP1 : oP0) + 4 * (btile & 1);
+      id0 += vlane;
+    }
+    uint64_t key = (btile < 0) ? 0ull : argmax_key(bs, uint32_t(id0 + bi));
     if constexpr (!GUMBEL) {
       // every lane merges its own candidate: no cross-lane round trip
       if (b < B && key != 0ull)
@@ -292,13 +349,13 @@ struct TileWork {
   }
 
   __device__ __forceinline__ void run() const {
-    RawU<BF16> b0[NTF], b1[NTF], b2[NTF];
+    Buf b0, b1, b2;
     issue(b0, 0);
     issue(b1, 1);
     issue(b2, 2);
     // Straight-line loop body (the compiler's wait counts stay exact across
-    // the back edge: consuming a buffer waits only for its own five loads);
-    // the last one or two request tiles run after the loop.
+    // the back edge: consuming a buffer waits only for its own loads); the
+    // last one or two request tiles run after the loop.
     int bt = 0;
     for (; bt + 3 <= nbt; bt += 3) {
       step(b0, bt);
@@ -316,11 +373,14 @@ __device__ __forceinline__ void compute_tiles(const typename Elem<BF16>::frag_t 
                                               const typename Elem<BF16>::store_t* U, int g0, int rows, int B,
                                               int gamma, int k, int V, int w_lo, int nt, int vec_ok, int li, int lg,
                                               uint32_t seed_lo, uint32_t seed_hi, uint64_t* lds_key, float* lds_zw) {
-  const int vlane = w_lo * 16 + 4 * lg;
   const size_t row_stride = size_t(gamma) * V;
+  const int vlane = CHECKED ? w_lo * 16 + 4 * lg : w_lo * 16;
+  const int oP0 = CHECKED ? 0 : pair_col(0, lg, nt, TPW);
+  const int oP1 = CHECKED ? 0 : pair_col(2 < 2 * (TPW / 2) ? 2 : 0, lg, nt, TPW);
+  const int oL = CHECKED ? 0 : pair_col(TPW - 1, lg, nt, TPW);
   TileWork<BF16, R, TPW, GR, GUMBEL, NTF, CHECKED> w{
-      A, lds_e, U, lds_key, lds_zw, row_stride, U + (size_t(g0) * gamma + (k - 1)) * V + vlane,
-      g0, rows, (rows + 15) >> 4, B, k, V, w_lo, nt, vec_ok, li, lg, vlane, seed_lo, seed_hi};
+      A, lds_e, lds_key, lds_zw, row_stride, U + (size_t(g0) * gamma + (k - 1)) * V + vlane,
+      g0, rows, (rows + 15) >> 4, B, k, V, nt, vec_ok, li, lg, vlane, oP0, oP1, oL, seed_lo, seed_hi};
   w.run();
 }
 
@@ -371,8 +431,9 @@ __device__ __forceinline__ double hidden_dot(const float* row, const float* w, i
   return wave_sum_f64(acc);
 }
 
-// FULL: V % 16 == 0, every vocabulary tile is whole and rows are 8-byte
-// aligned, so the branch-free tile path is used; otherwise the guarded path.
+// FULL (bf16 only): V % 16 == 0, so every vocabulary tile is whole and rows
+// are 32-byte aligned, and every wave owns either no tile or at least two,
+// so the branch-free pair layout applies; otherwise the guarded path.
 template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL>
 __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p) {
   typedef Elem<BF16> E;
@@ -473,8 +534,9 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       __syncthreads();
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        if (nt > 0) {   // tiles past the wave's range repeat its last tile
-          const int c = (w_lo - wg_lo + min(t, nt - 1)) * 16 + li;
+        if (nt > 0) {   // spare slots repeat columns the wave owns (pair layout when FULL)
+          const int c = (w_lo - wg_lo) * 16 +
+                        (FULL ? pair_col(t, li >> 2, nt, TPW) + (li & 3) : min(t, nt - 1) * 16 + li);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const int kr = ks * E::KS + E::KPL * lg - kc;   // kn is a multiple of KS: kr..kr+KPL-1 all staged
@@ -660,9 +722,11 @@ struct KernelChoice {
   int tpw;
 };
 
+constexpr int kDraftWaves = 8;
+
 template <bool BF16, int R, bool G>
 KernelChoice pick_r(bool full) {
-  constexpr int NW = 8, GR = 256;
+  constexpr int NW = kDraftWaves, GR = 256;
   constexpr int TPW = BF16 ? 5 : 4;
   if constexpr (BF16) {
     if (full)
@@ -734,14 +798,6 @@ DraftWorkspace draft_workspace_layout(int B, int gamma) {
 
 hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported) {
   *unsupported = nullptr;
-  KernelChoice kc;
-  const bool full = (a.V % 16) == 0;
-  const bool ok = a.gumbel ? pick<true>(a.bf16, a.r, full, &kc) : pick<false>(a.bf16, a.r, full, &kc);
-  if (!ok) {
-    *unsupported = a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
-                          : "fp32 drafting supports r in {16, 32, 64}";
-    return hipSuccess;
-  }
   DeviceInfo info;
   hipError_t e = device_info(&info);
   if (e != hipSuccess) return e;
@@ -749,6 +805,15 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   int nwg = info.cus < kMaxDraftWorkgroups ? info.cus : kMaxDraftWorkgroups;
   if (nwg > tiles) nwg = tiles;
   if (nwg < 1) nwg = 1;
+  // the pair layout needs at least two tiles in every wave's range
+  const bool full = (a.V % 16) == 0 && (tiles / nwg) / kDraftWaves >= 2;
+  KernelChoice kc;
+  const bool ok = a.gumbel ? pick<true>(a.bf16, a.r, full, &kc) : pick<false>(a.bf16, a.r, full, &kc);
+  if (!ok) {
+    *unsupported = a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
+                          : "fp32 drafting supports r in {16, 32, 64}";
+    return hipSuccess;
+  }
   const int per_wg = (tiles + nwg - 1) / nwg;
   const int nwaves = kc.threads / 64;
   if ((per_wg + nwaves - 1) / nwaves > kc.tpw) {

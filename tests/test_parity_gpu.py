@@ -118,6 +118,20 @@ def test_small_gumbel(shape):
     end_to_end(w, d, out)
 
 
+@pytest.mark.parametrize("V,sampling", [(70016, "greedy"), (100000, "greedy"), (131072, "greedy"),
+                                        (100000, "gumbel")])
+def test_vocab_splits_of_the_whole_tile_path(V, sampling):
+    """V % 16 == 0 and at least two tiles per wave: the branch-free path with
+    paired tiles.  On a 256-CU GPU these vocabularies give waves owning
+    {2, 3}, {3, 4} and exactly 4 tiles, so every spare-slot case is covered."""
+    cfg = wl.small_config(B=24, gamma=3, V=V, r=256, d=64, dtype="bf16", sampling=sampling)
+    w = wl.make_workload(cfg)
+    if sampling == "gumbel":
+        w["seed"] = 0xBADC0FFEE
+    d, out = run_case(w)
+    end_to_end(w, d, out)
+
+
 def test_small_weak_plant_many_near_ties():
     """No plant: logits are pure noise, so near ties and replays are routine."""
     cfg = wl.small_config(B=64, gamma=4, V=20000, r=64, d=16, dtype="bf16", plant=(0.0, 0.0))
