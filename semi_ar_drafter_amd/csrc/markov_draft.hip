@@ -798,6 +798,12 @@ DraftWorkspace draft_workspace_layout(int B, int gamma) {
 
 hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported) {
   *unsupported = nullptr;
+  KernelChoice kc;
+  if (!(a.gumbel ? pick<true>(a.bf16, a.r, false, &kc) : pick<false>(a.bf16, a.r, false, &kc))) {
+    *unsupported = a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
+                          : "fp32 drafting supports r in {16, 32, 64}";
+    return hipSuccess;
+  }
   DeviceInfo info;
   hipError_t e = device_info(&info);
   if (e != hipSuccess) return e;
@@ -807,12 +813,11 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   if (nwg < 1) nwg = 1;
   // the pair layout needs at least two tiles in every wave's range
   const bool full = (a.V % 16) == 0 && (tiles / nwg) / kDraftWaves >= 2;
-  KernelChoice kc;
-  const bool ok = a.gumbel ? pick<true>(a.bf16, a.r, full, &kc) : pick<false>(a.bf16, a.r, full, &kc);
-  if (!ok) {
-    *unsupported = a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
-                          : "fp32 drafting supports r in {16, 32, 64}";
-    return hipSuccess;
+  if (full) {
+    if (a.gumbel)
+      pick<true>(a.bf16, a.r, true, &kc);
+    else
+      pick<false>(a.bf16, a.r, true, &kc);
   }
   const int per_wg = (tiles + nwg - 1) / nwg;
   const int nwaves = kc.threads / 64;
