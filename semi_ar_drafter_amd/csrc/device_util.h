@@ -71,6 +71,17 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
   return -logf(-logf(u));
 }
 
+// 16-byte direct-to-LDS load (gfx950 global_load_lds_dwordx4): lane j of the
+// wave copies 16 bytes from its own global address `src` to lds_base + 16 * j.
+// lds_base must be the same for every lane.  Completion is tracked by the
+// vector-memory counter only (see wait_vmem); the compiler does not order
+// later LDS reads after it, so readers synchronise explicitly.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+#endif
+}
+
 // Waits until this wave's outstanding vector-memory operations (loads,
 // stores, atomics) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -88,18 +99,22 @@ __device__ __forceinline__ void store_dev(T* p, T v) {
 
 // Grid-wide barrier for a co-resident (cooperatively launched) grid whose
 // cross-workgroup data moves only through device-scope atomics, loads and
-// stores: every wave waits for its own memory operations to complete, the
-// workgroup synchronises, and one thread arrives on the counter and polls
-// it.  The counter counts arrivals over the whole launch; barrier number n
-// waits for n * gridDim.x arrivals.  The spin is bounded: after `limit`
-// polls the error flag is raised, and once it is raised every barrier
-// returns at once, so every wave always reaches the end of the kernel.
-__device__ __forceinline__ void grid_barrier(unsigned int* counter, unsigned int* err,
-                                             unsigned int target, unsigned int limit) {
+// stores, in two halves so that independent work can be issued in between.
+// grid_arrive: every wave waits for its own memory operations to complete,
+// the workgroup synchronises, and one thread arrives on the counter.
+// grid_wait: that thread polls the counter; the workgroup synchronises.  The
+// counter counts arrivals over the whole launch; barrier number n waits for
+// n * gridDim.x arrivals.  The spin is bounded: after `limit` polls the
+// error flag is raised, and once it is raised every barrier returns at once,
+// so every wave always reaches the end of the kernel.
+__device__ __forceinline__ void grid_arrive(unsigned int* counter) {
   wait_vmem();
   __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void grid_wait(unsigned int* counter, unsigned int* err, unsigned int target,
+                                          unsigned int limit) {
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned int polls = 0;
     while (load_dev(counter) < target) {
       if (load_dev(err) != 0u) break;

@@ -82,6 +82,27 @@ struct Elem<false> {
   static constexpr int PAD = 4;
 };
 
+// Layout of the gathered embeddings e in LDS.  bf16 rows are stored
+// unpadded (R elements) and filled by 16-byte direct-to-LDS loads; the
+// 16-byte chunks of a row are permuted by an XOR with a per-row code so that
+// the B-operand reads of 8 consecutive rows fall on 8 different bank groups.
+// fp32 rows are padded instead.
+template <bool BF16, int R>
+struct ELayout {
+  static constexpr int LDE = BF16 ? R : R + Elem<BF16>::PAD;                      // row stride (elements)
+  static constexpr int CPR = R * int(sizeof(typename Elem<BF16>::store_t)) / 16;  // 16-byte chunks per row
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (!BF16) return 0;
+    else if constexpr (CPR >= 8) return row & 7;
+    else return (row / (8 / CPR)) & (CPR - 1);
+  }
+  // offset (elements) of element i of row `row`
+  __device__ static __forceinline__ int at(int row, int i) {
+    if constexpr (!BF16) return row * LDE + i;
+    else return row * LDE + (((i >> 3) ^ swz(row)) << 3) + (i & 7);
+  }
+};
+
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -195,7 +216,8 @@ struct TileWork {
   typedef typename E::store_t st_t;
   typedef typename E::frag_t frag_t;
   static constexpr int NKS = R / E::KS;
-  static constexpr int LDE = R + E::PAD;
+  typedef ELayout<BF16, R> EL;
+  static constexpr int LDE = EL::LDE;
   static constexpr int NP = TPW / 2;               // tile pairs (unchecked form)
   static constexpr bool LONE = (TPW & 1) != 0;     // unpaired last slot
   static_assert(CHECKED || (BF16 && NTF == TPW), "the pair layout is for bf16 whole tiles");
@@ -218,7 +240,19 @@ struct TileWork {
   int g0, rows, nbt, B, k, V, nt, vec_ok, li, lg;
   int vlane;           // CHECKED: first id of this lane's 4 in tile 0; else the wave's first column
   int oP0, oP1, oL;    // unchecked: columns (relative) of this lane's pair-0 / pair-1 / last-slot loads
+  int fe, fo;          // bf16: offsets within a row of this lane's B fragment for even / odd K steps
   uint32_t seed_lo, seed_hi;
+
+  // B-operand fragment of request tile bt, K step ks (ks is a compile-time constant after unrolling).
+  // bf16: chunk (4 ks + lg) of row bt*16 + li sits at chunk ((4 ks + lg) ^ swz(li)); with
+  // s = swz(li) that is 4 (ks ^ (s >> 2)) + (lg ^ (s & 3)), i.e. a per-lane base for even and
+  // for odd ks plus 64 (ks >> 1) elements.
+  __device__ __forceinline__ frag_t bfrag(int bt, int ks) const {
+    if constexpr (BF16)
+      return lds_frag(lds_e + (bt * 16 + li) * LDE + ((ks & 1) ? fo : fe) + 64 * (ks >> 1));
+    else
+      return lds_frag(lds_e + (bt * 16 + li) * LDE + ks * E::KS + E::KPL * lg);
+  }
 
   // first of this lane's four consecutive ids in tile slot t
   __device__ __forceinline__ int tile_id0(int t) const {
@@ -264,12 +298,11 @@ struct TileWork {
     f32x4_t acc[NTF];
     widen(bb, acc);
     issue(bb, bt + 3);
-    const st_t* erow = lds_e + (bt * 16 + li) * LDE + E::KPL * lg;
-    frag_t bfr = lds_frag(erow);
+    frag_t bfr = bfrag(bt, 0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const frag_t cur = bfr;
-      if (ks + 1 < NKS) bfr = lds_frag(erow + (ks + 1) * E::KS);
+      if (ks + 1 < NKS) bfr = bfrag(bt, ks + 1);
 #pragma unroll
       for (int t = 0; t < NTF; ++t) {
         if constexpr (CHECKED) {
@@ -348,11 +381,16 @@ struct TileWork {
     }
   }
 
-  __device__ __forceinline__ void run() const {
-    Buf b0, b1, b2;
+  // First three request tiles' loads, issued ahead of run() (possibly
+  // before the grid barrier that precedes the step: U does not depend on
+  // the drafted tokens).
+  __device__ __forceinline__ void prefetch(Buf& b0, Buf& b1, Buf& b2) const {
     issue(b0, 0);
     issue(b1, 1);
     issue(b2, 2);
+  }
+
+  __device__ __forceinline__ void run(Buf& b0, Buf& b1, Buf& b2) const {
     // Straight-line loop body (the compiler's wait counts stay exact across
     // the back edge: consuming a buffer waits only for its own loads); the
     // last one or two request tiles run after the loop.
@@ -368,20 +406,21 @@ struct TileWork {
 };
 
 template <bool BF16, int R, int TPW, int GR, bool GUMBEL, int NTF, bool CHECKED>
-__device__ __forceinline__ void compute_tiles(const typename Elem<BF16>::frag_t (&A)[TPW][R / Elem<BF16>::KS],
-                                              const typename Elem<BF16>::store_t* lds_e,
-                                              const typename Elem<BF16>::store_t* U, int g0, int rows, int B,
-                                              int gamma, int k, int V, int w_lo, int nt, int vec_ok, int li, int lg,
-                                              uint32_t seed_lo, uint32_t seed_hi, uint64_t* lds_key, float* lds_zw) {
+__device__ __forceinline__ TileWork<BF16, R, TPW, GR, GUMBEL, NTF, CHECKED> make_work(
+    const typename Elem<BF16>::frag_t (&A)[TPW][R / Elem<BF16>::KS], const typename Elem<BF16>::store_t* lds_e,
+    const typename Elem<BF16>::store_t* U, int g0, int rows, int B, int gamma, int k, int V, int w_lo, int nt,
+    int vec_ok, int li, int lg, uint32_t seed_lo, uint32_t seed_hi, uint64_t* lds_key, float* lds_zw) {
   const size_t row_stride = size_t(gamma) * V;
   const int vlane = CHECKED ? w_lo * 16 + 4 * lg : w_lo * 16;
   const int oP0 = CHECKED ? 0 : pair_col(0, lg, nt, TPW);
   const int oP1 = CHECKED ? 0 : pair_col(2 < 2 * (TPW / 2) ? 2 : 0, lg, nt, TPW);
   const int oL = CHECKED ? 0 : pair_col(TPW - 1, lg, nt, TPW);
-  TileWork<BF16, R, TPW, GR, GUMBEL, NTF, CHECKED> w{
+  const int sw = ELayout<BF16, R>::swz(li);
+  const int m = lg ^ (sw & 3), h = sw >> 2;
+  return TileWork<BF16, R, TPW, GR, GUMBEL, NTF, CHECKED>{
       A, lds_e, lds_key, lds_zw, row_stride, U + (size_t(g0) * gamma + (k - 1)) * V + vlane,
-      g0, rows, (rows + 15) >> 4, B, k, V, nt, vec_ok, li, lg, vlane, oP0, oP1, oL, seed_lo, seed_hi};
-  w.run();
+      g0, rows, (rows + 15) >> 4, B, k, V, nt, vec_ok, li, lg, vlane, oP0, oP1, oL,
+      8 * (4 * h + m), 8 * (4 * (1 - h) + m), seed_lo, seed_hi};
 }
 
 // Hidden-state half of the confidence logit, hdot[b][k] = sum_j conf_w[j] *
@@ -440,7 +479,8 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   typedef typename E::store_t st_t;
   typedef typename E::frag_t frag_t;
   constexpr int NKS = R / E::KS;
-  constexpr int LDE = R + E::PAD;
+  typedef ELayout<BF16, R> EL;
+  constexpr int LDE = EL::LDE;
   constexpr int NT = NW * 64;
   constexpr int CHUNKS = int(R * sizeof(st_t)) / 16;      // 16-byte pieces per W1 row
   static_assert(R % E::KS == 0, "rank must be a multiple of the MFMA K step");
@@ -578,27 +618,37 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     return int(x);
   };
 
+  // The next group's first three request tiles of U are loaded ahead of
+  // time, before the slot reads and the gather that precede their use.
+  typedef TileWork<BF16, R, TPW, GR, GUMBEL, TPW, !FULL> Work;
+  auto work = [&](int k, int g0, int rows) {
+    return make_work<BF16, R, TPW, GR, GUMBEL, TPW, !FULL>(A, lds_e, U, g0, rows, B, gamma, k, V, w_lo, nt,
+                                                           p.vec_ok, li, lg, p.seed_lo, p.seed_hi, lds_key,
+                                                           lds_z[wave]);
+  };
+  typename Work::Buf pf0, pf1, pf2;
+  if (nt > 0) work(1, 0, min(GR, B)).prefetch(pf0, pf1, pf2);
+
   for (int k = 1; k <= gamma; ++k) {
     for (int grp = 0; grp < ngroups; ++grp) {
       const int g0 = grp * GR;
       const int rows = min(GR, B - g0);
 
-      // 1. previous tokens of the group's rows (and the outputs of step k-1)
+      // 1. previous tokens of the group's rows
+      uint64_t own_key = 0ull;   // key of step k-1 for a row this workgroup owns (emitted below)
+      bool own = false;
       if (tid < rows) {
         const int b = g0 + tid;
-        const bool own = (b % nwg) == wg;
+        own = (b % nwg) == wg;
         int x;
         if (k == 1) {
           x = min(max(int(p.anchor[b]), 0), V - 1);
         } else {
           const uint64_t key = __hip_atomic_load(&p.slots[size_t(k - 2) * B + b], __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-          if (own) {
-            x = emit(b, k - 1, key);
-          } else {
-            x = int(key_index(key));
-            if (key == 0ull || x >= V || x < 0) x = V - 1;
-          }
+          own_key = key;
+          x = int(key_index(key));
+          if (key == 0ull || x >= V || x < 0) x = V - 1;
         }
         lds_x[tid] = x;
         if (own) lds_hd[tid] = load_dev(&p.hdot[size_t(b) * gamma + (k - 1)]);
@@ -606,42 +656,48 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       __syncthreads();
 
       // 2. gather e = W1[x_{k-1}] for the group's rows into LDS
-      // (eight 16-byte loads in flight per thread before their LDS stores)
-      for (int c0 = tid; c0 < GR * CHUNKS; c0 += 8 * NT) {
-        u32x4_t val[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = c0 + u * NT;
-          const int row = c / CHUNKS, ch = c - row * CHUNKS;
-          val[u] = u32x4_t{0u, 0u, 0u, 0u};
-          if (c < GR * CHUNKS && row < rows)
-            val[u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(W1 + size_t(lds_x[row]) * R) +
-                                                       ch * 16);
+      if constexpr (BF16) {
+        // one 16-byte direct-to-LDS load per lane, 64 / CPR rows per instruction, all in flight at once;
+        // lane -> (row, physical chunk p) holds logical chunk p ^ swz(row); rows past the group read row 0
+        constexpr int CPR = EL::CPR;
+        constexpr int RPI = 64 / CPR;
+        static_assert(RPI * CPR == 64 && GR % RPI == 0, "gather instruction shape");
+        for (int i = wave; i < GR / RPI; i += NW) {
+          const int row = i * RPI + lane / CPR;
+          const int x = row < rows ? lds_x[row] : 0;
+          const int c = (lane % CPR) ^ EL::swz(row);
+          load_lds16(W1 + size_t(x) * R + c * 8, lds_e + i * RPI * R);
         }
+      } else {
+        // eight 16-byte loads in flight per thread before their LDS stores
+        for (int c0 = tid; c0 < GR * CHUNKS; c0 += 8 * NT) {
+          u32x4_t val[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = c0 + u * NT;
-          const int row = c / CHUNKS, ch = c - row * CHUNKS;
-          if (c < GR * CHUNKS) *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(lds_e + row * LDE) + ch * 16) = val[u];
+          for (int u = 0; u < 8; ++u) {
+            const int c = c0 + u * NT;
+            const int row = c / CHUNKS, ch = c - row * CHUNKS;
+            val[u] = u32x4_t{0u, 0u, 0u, 0u};
+            if (c < GR * CHUNKS && row < rows)
+              val[u] = *reinterpret_cast<const u32x4_t*>(
+                  reinterpret_cast<const char*>(W1 + size_t(lds_x[row]) * R) + ch * 16);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int c = c0 + u * NT;
+            const int row = c / CHUNKS, ch = c - row * CHUNKS;
+            if (c < GR * CHUNKS)
+              *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(lds_e + row * LDE) + ch * 16) = val[u];
+          }
         }
       }
+      // outputs of step k-1 for owned rows, overlapping the gather
+      if (own && k > 1) emit(g0 + tid, k - 1, own_key);
+      wait_vmem();   // this wave's direct-to-LDS loads have landed
       __syncthreads();
 
       // 4. z = U_k + e W2 on MFMA, argmax in registers, per request tile
-      {
-        // Whole tiles: branch-free path over exactly TPW tiles (a wave with
-        // fewer tiles repeats its last one, whose equal scores at the same ids
-        // never win the strict comparison).
-        if (nt > 0) {
-          if constexpr (FULL)
-            compute_tiles<BF16, R, TPW, GR, GUMBEL, TPW, false>(A, lds_e, U, g0, rows, B, gamma, k, V, w_lo, nt,
-                                                                p.vec_ok, li, lg, p.seed_lo, p.seed_hi, lds_key,
-                                                                lds_z[wave]);
-          else
-            compute_tiles<BF16, R, TPW, GR, GUMBEL, TPW, true>(A, lds_e, U, g0, rows, B, gamma, k, V, w_lo, nt,
-                                                               p.vec_ok, li, lg, p.seed_lo, p.seed_hi, lds_key,
-                                                               lds_z[wave]);
-        }
+      if (nt > 0) {
+        work(k, g0, rows).run(pf0, pf1, pf2);
       }
 
       // 3. confidence + STS + survival for the rows this workgroup owns (after the
@@ -653,7 +709,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           const int b = wg + j * nwg;
           const int row = b - g0;
           double acc = 0.0;
-          for (int i = lane; i < R; i += 64) acc += double(lds_we[i]) * double(to_f32(lds_e[row * LDE + i]));
+          for (int i = lane; i < R; i += 64) acc += double(lds_we[i]) * double(to_f32(lds_e[EL::at(row, i)]));
           acc = wave_sum_f64(acc);
           if (lane == 0) {
             const double ell = double(p.conf_b) + (lds_hd[row] + acc);
@@ -683,8 +739,13 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
         }
       }
       __syncthreads();
+      if (grp + 1 < ngroups && nt > 0) work(k, g0 + GR, min(GR, B - g0 - GR)).prefetch(pf0, pf1, pf2);
     }
-    grid_barrier(&p.ctrl[0], &p.ctrl[1], unsigned(k) * unsigned(nwg), p.spin_limit);
+    grid_arrive(&p.ctrl[0]);
+    grid_wait(&p.ctrl[0], &p.ctrl[1], unsigned(k) * unsigned(nwg), p.spin_limit);
+    // (issued only after the barrier: loads issued while slower workgroups are
+    // still computing the step take bandwidth from them and lengthen the step)
+    if (k < gamma && nt > 0) work(k + 1, 0, min(GR, B)).prefetch(pf0, pf1, pf2);
   }
   // outputs of the last step; a failed synchronisation marks every token -1
   const bool failed = load_dev(&p.ctrl[1]) != 0u;
