@@ -11,6 +11,11 @@ namespace dspark {
 constexpr int kMaxDraftWorkgroups = 512;
 // Largest number of requests one workgroup can own for the confidence epilogue.
 constexpr int kMaxOwnedRows = 64;
+// Requests per group in the draft kernel (LDS holds one group's embeddings).
+constexpr int kMaxGroupRows = 128;
+// Distance (in 32-bit words) between the per-group arrival counters (one
+// 128-byte line each: every workgroup polls them).
+constexpr int kBarStride = 32;
 // Scheduler: one workgroup sorts all (request, position) keys in LDS.
 constexpr int kMaxScheduleItems = 16384;
 
@@ -31,7 +36,7 @@ struct DraftArgs {
 
 // Workspace carve-up of the draft call (byte offsets, 256-aligned).
 struct DraftWorkspace {
-  size_t ctrl, slots, zpart, hdot, total;
+  size_t ctrl, bar, slots, zpart, hdot, total;
 };
 DraftWorkspace draft_workspace_layout(int B, int gamma);
 

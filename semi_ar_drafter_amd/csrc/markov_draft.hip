@@ -57,7 +57,9 @@ struct DraftParams {
   float* logit;
   float* conf;
   float* surv;
-  unsigned int* ctrl;  // [0] barrier arrivals, [1] error flag, [2] exit arrivals
+  int grs;             // requests per group (multiple of 16, at most the kernel's GR)
+  unsigned int* ctrl;  // [1] error flag, [2] exit arrivals
+  unsigned int* bar;   // arrivals of request group g at bar[g * kBarStride]
   uint64_t* slots;     // [gamma][B] packed argmax keys
   float* zpart;        // [2][nwg][B] logit of each workgroup's local winner
   double* hdot;        // [B][gamma] hidden-state part of the confidence logit
@@ -509,9 +511,9 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   const int w_lo = wg_lo + part_start(wave, wg_nt, NW);
   const int nt = wg_lo + part_start(wave + 1, wg_nt, NW) - w_lo;   // <= TPW
 
-  // A workspace left by a completed call has a zero barrier counter; before
+  // A workspace left by a completed call has zero barrier counters; before
   // this workgroup's first arrival at most nwg - 1 others can have arrived.
-  if (tid == 0 && load_dev(&p.ctrl[0]) >= unsigned(nwg)) store_dev(&p.ctrl[1], 2u);
+  if (tid == 0 && load_dev(&p.bar[0]) >= unsigned(nwg)) store_dev(&p.ctrl[1], 2u);
 
   // hdot for every (owned request, position): one (b, k) per wave at a time.
   {
@@ -603,7 +605,8 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
 
   const st_t* U = static_cast<const st_t*>(p.U);
   const st_t* W1 = static_cast<const st_t*>(p.W1);
-  const int ngroups = (B + GR - 1) / GR;
+  const int grs = p.grs;
+  const int ngroups = (B + grs - 1) / grs;
 
   // Publishes the drafted token of step kk (1-based) for a row this
   // workgroup owns; its logit comes from the workgroup whose tiles hold it.
@@ -618,6 +621,14 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     return int(x);
   };
 
+  // Requests are processed in groups of grs rows, group by group within a
+  // step.  Each group has its own arrival counter: step k of group g needs
+  // only the tokens of step k-1 of group g, so while the slowest workgroups
+  // finish a group, the others already compute the next group instead of
+  // waiting.  A workgroup's arrival for a group is issued after the next
+  // group's gather, whose completion wait also covers the publishing atomics
+  // (with a single group it is issued at once).
+  //
   // The next group's first three request tiles of U are loaded ahead of
   // time, before the slot reads and the gather that precede their use.
   typedef TileWork<BF16, R, TPW, GR, GUMBEL, TPW, !FULL> Work;
@@ -626,13 +637,18 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
                                                            p.vec_ok, li, lg, p.seed_lo, p.seed_hi, lds_key,
                                                            lds_z[wave]);
   };
+  auto bar = [&](int g) { return p.bar + size_t(g) * kBarStride; };
   typename Work::Buf pf0, pf1, pf2;
-  if (nt > 0) work(1, 0, min(GR, B)).prefetch(pf0, pf1, pf2);
+  if (nt > 0) work(1, 0, min(grs, B)).prefetch(pf0, pf1, pf2);
+  int pending = -1;   // group whose arrival is still to be issued
 
   for (int k = 1; k <= gamma; ++k) {
     for (int grp = 0; grp < ngroups; ++grp) {
-      const int g0 = grp * GR;
-      const int rows = min(GR, B - g0);
+      const int g0 = grp * grs;
+      const int rows = min(grs, B - g0);
+
+      // tokens of step k-1 of this group are final once every workgroup has arrived
+      if (k > 1) grid_wait(bar(grp), &p.ctrl[1], unsigned(k - 1) * unsigned(nwg), p.spin_limit);
 
       // 1. previous tokens of the group's rows
       uint64_t own_key = 0ull;   // key of step k-1 for a row this workgroup owns (emitted below)
@@ -655,14 +671,15 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       }
       __syncthreads();
 
-      // 2. gather e = W1[x_{k-1}] for the group's rows into LDS
+      // 2. gather e = W1[x_{k-1}] for the group's rows (rounded up to whole request tiles) into LDS
+      const int rows16 = (rows + 15) & ~15;
       if constexpr (BF16) {
         // one 16-byte direct-to-LDS load per lane, 64 / CPR rows per instruction, all in flight at once;
         // lane -> (row, physical chunk p) holds logical chunk p ^ swz(row); rows past the group read row 0
         constexpr int CPR = EL::CPR;
         constexpr int RPI = 64 / CPR;
-        static_assert(RPI * CPR == 64 && GR % RPI == 0, "gather instruction shape");
-        for (int i = wave; i < GR / RPI; i += NW) {
+        static_assert(RPI * CPR == 64 && 16 % RPI == 0, "gather instruction shape");
+        for (int i = wave; i < rows16 / RPI; i += NW) {
           const int row = i * RPI + lane / CPR;
           const int x = row < rows ? lds_x[row] : 0;
           const int c = (lane % CPR) ^ EL::swz(row);
@@ -670,14 +687,14 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
         }
       } else {
         // eight 16-byte loads in flight per thread before their LDS stores
-        for (int c0 = tid; c0 < GR * CHUNKS; c0 += 8 * NT) {
+        for (int c0 = tid; c0 < rows16 * CHUNKS; c0 += 8 * NT) {
           u32x4_t val[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const int c = c0 + u * NT;
             const int row = c / CHUNKS, ch = c - row * CHUNKS;
             val[u] = u32x4_t{0u, 0u, 0u, 0u};
-            if (c < GR * CHUNKS && row < rows)
+            if (c < rows16 * CHUNKS && row < rows)
               val[u] = *reinterpret_cast<const u32x4_t*>(
                   reinterpret_cast<const char*>(W1 + size_t(lds_x[row]) * R) + ch * 16);
           }
@@ -685,20 +702,22 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           for (int u = 0; u < 8; ++u) {
             const int c = c0 + u * NT;
             const int row = c / CHUNKS, ch = c - row * CHUNKS;
-            if (c < GR * CHUNKS)
+            if (c < rows16 * CHUNKS)
               *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(lds_e + row * LDE) + ch * 16) = val[u];
           }
         }
       }
       // outputs of step k-1 for owned rows, overlapping the gather
       if (own && k > 1) emit(g0 + tid, k - 1, own_key);
-      wait_vmem();   // this wave's direct-to-LDS loads have landed
+      wait_vmem();   // this wave's direct-to-LDS loads have landed (and its earlier atomics are done)
       __syncthreads();
+      if (pending >= 0) {
+        if (tid == 0) __hip_atomic_fetch_add(bar(pending), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pending = -1;
+      }
 
       // 4. z = U_k + e W2 on MFMA, argmax in registers, per request tile
-      if (nt > 0) {
-        work(k, g0, rows).run(pf0, pf1, pf2);
-      }
+      if (nt > 0) work(k, g0, rows).run(pf0, pf1, pf2);
 
       // 3. confidence + STS + survival for the rows this workgroup owns (after the
       //    MFMA phase: it only needs e, which stays in LDS until the next gather)
@@ -738,15 +757,23 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           store_dev(&p.zpart[(size_t((k & 1) * nwg + wg)) * B + b], GUMBEL ? lds_z[w][tid] : key_value(key));
         }
       }
-      __syncthreads();
-      if (grp + 1 < ngroups && nt > 0) work(k, g0 + GR, min(GR, B - g0 - GR)).prefetch(pf0, pf1, pf2);
+      const bool last = (k == gamma) && (grp + 1 == ngroups);
+      if (ngroups == 1 || last) {
+        grid_arrive(bar(grp));
+      } else {
+        pending = grp;
+        __syncthreads();
+      }
+      if (!last && nt > 0) {
+        const int nk = (grp + 1 < ngroups) ? k : k + 1;
+        const int ng0 = (grp + 1 < ngroups) ? g0 + grs : 0;
+        work(nk, ng0, min(grs, B - ng0)).prefetch(pf0, pf1, pf2);
+      }
     }
-    grid_arrive(&p.ctrl[0]);
-    grid_wait(&p.ctrl[0], &p.ctrl[1], unsigned(k) * unsigned(nwg), p.spin_limit);
-    // (issued only after the barrier: loads issued while slower workgroups are
-    // still computing the step take bandwidth from them and lengthen the step)
-    if (k < gamma && nt > 0) work(k + 1, 0, min(GR, B)).prefetch(pf0, pf1, pf2);
   }
+  // every group's last step is final before its outputs are read
+  for (int g = 0; g < ngroups; ++g) grid_wait(bar(g), &p.ctrl[1], unsigned(gamma) * unsigned(nwg), p.spin_limit);
+
   // outputs of the last step; a failed synchronisation marks every token -1
   const bool failed = load_dev(&p.ctrl[1]) != 0u;
   for (int b = wg + tid * nwg; b < B; b += NT * nwg) {
@@ -769,8 +796,8 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     __syncthreads();
     const long long nslots = (long long)gamma * B;
     for (long long i = tid; i < nslots; i += NT) store_dev(&p.slots[i], uint64_t(0));
+    for (int g = tid; g < ngroups; g += NT) store_dev(bar(g), 0u);
     if (tid == 0) {
-      store_dev(&p.ctrl[0], 0u);
       store_dev(&p.ctrl[1], 0u);
       store_dev(&p.ctrl[2], 0u);
     }
@@ -787,7 +814,7 @@ constexpr int kDraftWaves = 8;
 
 template <bool BF16, int R, bool G>
 KernelChoice pick_r(bool full) {
-  constexpr int NW = kDraftWaves, GR = 256;
+  constexpr int NW = kDraftWaves, GR = kMaxGroupRows;
   constexpr int TPW = BF16 ? 5 : 4;
   if constexpr (BF16) {
     if (full)
@@ -847,6 +874,8 @@ DraftWorkspace draft_workspace_layout(int B, int gamma) {
   size_t off = 0;
   w.ctrl = off;
   off += 256;
+  w.bar = off;
+  off = align256(off + size_t((B + 15) / 16) * kBarStride * sizeof(unsigned int));
   w.slots = off;
   off = align256(off + size_t(gamma) * B * sizeof(uint64_t));
   w.zpart = off;
@@ -916,6 +945,12 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   p.conf = a.conf;
   p.surv = a.surv;
   p.ctrl = reinterpret_cast<unsigned int*>(ws + L.ctrl);
+  p.bar = reinterpret_cast<unsigned int*>(ws + L.bar);
+  // two groups (each group's barrier completes while the other computes), at most kMaxGroupRows rows
+  int grs = ((a.B + 1) / 2 + 15) & ~15;
+  if (grs > kMaxGroupRows) grs = kMaxGroupRows;
+  if (grs < 16) grs = 16;
+  p.grs = grs;
   p.slots = reinterpret_cast<uint64_t*>(ws + L.slots);
   p.zpart = reinterpret_cast<float*>(ws + L.zpart);
   p.hdot = reinterpret_cast<double*>(ws + L.hdot);
