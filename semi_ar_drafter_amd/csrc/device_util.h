@@ -82,6 +82,25 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 #endif
 }
 
+// LDS 64-bit atomic max and 32-bit store issued as plain ds_* instructions.
+// The compiler does not see them as LDS accesses, so it does not make them
+// wait for unrelated direct-to-LDS loads still in flight; in exchange the
+// caller waits for them explicitly (lds_wait) before any other wave reads
+// the locations.
+typedef __attribute__((address_space(3))) uint64_t lds_u64_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
+__device__ __forceinline__ void lds_max_u64(uint64_t* p, uint64_t v) {
+  asm volatile("ds_max_u64 %0, %1" : : "v"((lds_u64_t*)p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store_f32(float* p, float v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"((lds_f32_t*)p), "v"(v) : "memory");
+}
+// Byte address of an LDS location, as ds_* instructions take it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
 // Waits until this wave's outstanding vector-memory operations (loads,
 // stores, atomics) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -204,14 +204,18 @@ __device__ __forceinline__ int pair_col(int t, int q, int nt, int tpw) {
 // the first of those four equal to the best score: the lowest vocabulary id
 // among equal maxima.
 //
-// The U loads of request tile bt + 3 are issued right after tile bt's
-// buffer has been widened into the accumulators, into that same buffer
-// (three fixed buffers, no rotation), with the tile index clamped at the end
-// so the issue never sits behind a branch; the B-operand fragment is read
-// one K step ahead.  CHECKED (natural 16-wide tiles) handles a wave with
-// fewer than NTF tiles, a tile crossing the end of the vocabulary and V % 4
-// != 0; the unchecked form (bf16, whole tiles, the pair layout above) has no
-// per-tile branches.
+// The U loads of request tile bt + 3 are issued right after tile bt's data
+// has been taken into the accumulators, into the same one of three fixed
+// buffers, with the tile index clamped at the end so the issue never sits
+// behind a branch; the B-operand fragment is read one K step ahead.  CHECKED
+// (natural 16-wide tiles, U loaded into registers) handles a wave with fewer
+// than NTF tiles, a tile crossing the end of the vocabulary and V % 4 != 0.
+// The unchecked form (bf16, whole tiles, the pair layout above) has no
+// per-tile branches and stages U through a per-wave ring of three LDS slots:
+// the 16 rows x nt*32 bytes of a request tile are fetched row-major with
+// 16-byte direct-to-LDS loads (whole 128-byte lines per row, three load
+// instructions per tile), rows padded to an odd number of 16-byte chunks so
+// that the fragment reads of 8 consecutive rows hit 8 different bank groups.
 template <bool BF16, int R, int TPW, int GR, bool GUMBEL, int NTF, bool CHECKED>
 struct TileWork {
   typedef Elem<BF16> E;
@@ -227,11 +231,9 @@ struct TileWork {
   struct CheckedBuf {
     RawU<BF16> t[NTF];
   };
-  struct PairBuf {
-    u32x4_t p[NP > 0 ? NP : 1];
-    u32x2_t l;
-  };
-  typedef typename std::conditional<CHECKED, CheckedBuf, PairBuf>::type Buf;
+  struct SlotBuf {};   // the data lives in the wave's LDS slot of the same index
+  typedef typename std::conditional<CHECKED, CheckedBuf, SlotBuf>::type Buf;
+  static constexpr int SLOT_U32 = 768;   // one LDS slot: 192 16-byte chunks
 
   const frag_t (&A)[TPW][NKS];
   const st_t* lds_e;
@@ -243,6 +245,10 @@ struct TileWork {
   int vlane;           // CHECKED: first id of this lane's 4 in tile 0; else the wave's first column
   int oP0, oP1, oL;    // unchecked: columns (relative) of this lane's pair-0 / pair-1 / last-slot loads
   int fe, fo;          // bf16: offsets within a row of this lane's B fragment for even / odd K steps
+  uint32_t* lds_u;     // unchecked: this wave's three staging slots
+  int dr0, dr1, dr2;   // unchecked: request row (within the tile) of this lane's chunk in load instruction 0/1/2
+  int dc0, dc1, dc2;   //            and its column (elements, relative to the wave's first column)
+  int rP0, rP1, rL;    // unchecked: byte offsets within a slot of this lane's pair-0 / pair-1 / last-slot data
   uint32_t seed_lo, seed_hi;
 
   // B-operand fragment of request tile bt, K step ks (ks is a compile-time constant after unrolling).
@@ -266,40 +272,74 @@ struct TileWork {
     }
   }
 
+  // CHECKED: load this lane's U values of request tile bt into registers.
   __device__ __forceinline__ void issue(Buf& bb, int bt) const {
-    const int r = min(min(bt, nbt - 1) * 16 + li, rows - 1);   // clamped into the group
-    const st_t* p = ubase + size_t(r) * row_stride;
     if constexpr (CHECKED) {
+      const int r = min(min(bt, nbt - 1) * 16 + li, rows - 1);   // clamped into the group
+      const st_t* p = ubase + size_t(r) * row_stride;
 #pragma unroll
       for (int t = 0; t < NTF; ++t)
         if (t < nt) load_u(bb.t[t], p - vlane, vlane + 16 * t, V, vec_ok);   // row start, column
-    } else {
-      const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-      static_assert(NP <= 2, "pair offsets kept for two pairs");
-      if constexpr (NP >= 1) bb.p[0] = *reinterpret_cast<const u32x4_t*>(q + oP0);
-      if constexpr (NP >= 2) bb.p[1] = *reinterpret_cast<const u32x4_t*>(q + oP1);
-      if constexpr (LONE) bb.l = *reinterpret_cast<const u32x2_t*>(q + oL);
     }
   }
 
-  __device__ __forceinline__ void widen(const Buf& bb, f32x4_t (&acc)[NTF]) const {
-    if constexpr (CHECKED) {
-#pragma unroll
-      for (int t = 0; t < NTF; ++t) acc[t] = widen_u(bb.t[t]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        acc[2 * j] = f32x4_t{bf16_lo(bb.p[j].x), bf16_hi(bb.p[j].x), bf16_lo(bb.p[j].y), bf16_hi(bb.p[j].y)};
-        acc[2 * j + 1] = f32x4_t{bf16_lo(bb.p[j].z), bf16_hi(bb.p[j].z), bf16_lo(bb.p[j].w), bf16_hi(bb.p[j].w)};
-      }
-      if constexpr (LONE) acc[TPW - 1] = f32x4_t{bf16_lo(bb.l.x), bf16_hi(bb.l.x), bf16_lo(bb.l.y), bf16_hi(bb.l.y)};
-    }
+  // Unchecked: staging slot s (0..2) of this wave.
+  __device__ __forceinline__ uint32_t* slot(int s) const { return lds_u + s * SLOT_U32; }
+
+  // Unchecked: fetch request tile bt into slot s (three 16-byte direct-to-LDS loads per lane).
+  __device__ __forceinline__ void stage(int s, int bt) const {
+    const int r0 = min(bt, nbt - 1) * 16;
+    uint32_t* sl = slot(s);
+    load_lds16(ubase + size_t(min(r0 + dr0, rows - 1)) * row_stride + dc0, sl);
+    load_lds16(ubase + size_t(min(r0 + dr1, rows - 1)) * row_stride + dc1, sl + 256);
+    load_lds16(ubase + size_t(min(r0 + dr2, rows - 1)) * row_stride + dc2, sl + 512);
   }
 
+  // Unchecked: this lane's 20 base logits of the tile in slot s, widened into
+  // the accumulators.  `ahead` later tiles (three loads each) were staged
+  // after this one and may still be in flight; every older load has landed
+  // once at most that many are outstanding (vector-memory operations of a
+  // wave complete in order).  The reads are written as plain ds_* so that
+  // the compiler does not add a wait for every staging load in flight, and
+  // they complete before the asm block ends, so the slot can be refilled
+  // right after.
+  __device__ __forceinline__ void unstage(int s, int ahead, f32x4_t (&acc)[NTF]) const {
+    static_assert(NP == 2 && LONE, "staging reads written for two pairs and a last slot");
+    const uint32_t base = lds_addr(slot(s));
+    const uint32_t a0 = base + rP0, a1 = base + rP1, a2 = base + rL;
+    u32x4_t q0, q1;
+    u32x2_t ql;
+#define DSPARK_UNSTAGE(WAIT)                                                                  \
+  asm volatile("s_waitcnt " WAIT "\n\tds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\t"        \
+               "ds_read_b64 %2, %5\n\ts_waitcnt lgkmcnt(0)"                                  \
+               : "=&v"(q0), "=&v"(q1), "=&v"(ql)                                            \
+               : "v"(a0), "v"(a1), "v"(a2)                                                  \
+               : "memory")
+    if (ahead >= 2)
+      DSPARK_UNSTAGE("vmcnt(6)");
+    else if (ahead == 1)
+      DSPARK_UNSTAGE("vmcnt(3)");
+    else
+      DSPARK_UNSTAGE("vmcnt(0)");
+#undef DSPARK_UNSTAGE
+    acc[0] = f32x4_t{bf16_lo(q0.x), bf16_hi(q0.x), bf16_lo(q0.y), bf16_hi(q0.y)};
+    acc[1] = f32x4_t{bf16_lo(q0.z), bf16_hi(q0.z), bf16_lo(q0.w), bf16_hi(q0.w)};
+    acc[2] = f32x4_t{bf16_lo(q1.x), bf16_hi(q1.x), bf16_lo(q1.y), bf16_hi(q1.y)};
+    acc[3] = f32x4_t{bf16_lo(q1.z), bf16_hi(q1.z), bf16_lo(q1.w), bf16_hi(q1.w)};
+    acc[4] = f32x4_t{bf16_lo(ql.x), bf16_hi(ql.x), bf16_lo(ql.y), bf16_hi(ql.y)};
+  }
+
+  // CHECKED: one request tile from registers, then the loads of tile bt + 3 into the same buffer.
   __device__ __forceinline__ void step(Buf& bb, int bt) const {
     f32x4_t acc[NTF];
-    widen(bb, acc);
+#pragma unroll
+    for (int t = 0; t < NTF; ++t) acc[t] = widen_u(bb.t[t]);
     issue(bb, bt + 3);
+    tile(acc, bt);
+  }
+
+  // z = U + e W2 for request tile bt: the accumulators hold U on entry.
+  __device__ __forceinline__ void mfma_chain(f32x4_t (&acc)[NTF], int bt) const {
     frag_t bfr = bfrag(bt, 0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -314,8 +354,13 @@ struct TileWork {
         }
       }
     }
-    const int brow = bt * 16 + li;
-    const int b = g0 + brow;
+  }
+
+  // This lane's candidate for request tile bt (z, or z + Gumbel noise, in
+  // acc): the packed key (0 if none) and, for Gumbel sampling, the winner's
+  // unperturbed logit, already reduced over the lane groups.
+  __device__ __forceinline__ uint64_t select(const f32x4_t (&acc)[NTF], int bt, float& bz) const {
+    const int b = g0 + bt * 16 + li;
     float bs = -INFINITY;
     int btile = -1;
     f32x4_t bsel = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -360,14 +405,10 @@ struct TileWork {
       id0 += vlane;
     }
     uint64_t key = (btile < 0) ? 0ull : argmax_key(bs, uint32_t(id0 + bi));
-    if constexpr (!GUMBEL) {
-      // every lane merges its own candidate: no cross-lane round trip
-      if (b < B && key != 0ull)
-        __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(&lds_key[brow]), (unsigned long long)key,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else {
+    bz = 0.f;
+    if constexpr (GUMBEL) {
       // the winner's unperturbed logit travels with the key
-      float bz = (bi == 0) ? bzsel[0] : (bi == 1) ? bzsel[1] : (bi == 2) ? bzsel[2] : bzsel[3];
+      bz = (bi == 0) ? bzsel[0] : (bi == 1) ? bzsel[1] : (bi == 2) ? bzsel[2] : bzsel[3];
 #pragma unroll
       for (int m = 16; m <= 32; m <<= 1) {
         const uint64_t ok = shfl_xor_u64(key, m);
@@ -375,35 +416,64 @@ struct TileWork {
         if (ok > key) bz = oz;
         key = ok > key ? ok : key;
       }
-      if (lg == 0 && b < B && key != 0ull) {
-        __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(&lds_key[brow]), (unsigned long long)key,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        lds_zw[brow] = bz;
-      }
     }
+    return key;
+  }
+
+  // Merges a candidate of request tile bt into the workgroup's LDS key
+  // (greedy: every lane its own; Gumbel: lane group 0 after the reduction).
+  __device__ __forceinline__ void merge(uint64_t key, float bz, int bt) const {
+    const int brow = bt * 16 + li;
+    if (g0 + brow < B && key != 0ull && (!GUMBEL || lg == 0)) {
+      lds_max_u64(&lds_key[brow], key);
+      if constexpr (GUMBEL) lds_store_f32(&lds_zw[brow], bz);
+    }
+  }
+
+  __device__ __forceinline__ void tile(f32x4_t (&acc)[NTF], int bt) const {
+    mfma_chain(acc, bt);
+    float bz;
+    const uint64_t key = select(acc, bt, bz);
+    merge(key, bz, bt);
   }
 
   // First three request tiles' loads, issued ahead of run() (possibly
   // before the grid barrier that precedes the step: U does not depend on
   // the drafted tokens).
   __device__ __forceinline__ void prefetch(Buf& b0, Buf& b1, Buf& b2) const {
-    issue(b0, 0);
-    issue(b1, 1);
-    issue(b2, 2);
+    if constexpr (CHECKED) {
+      issue(b0, 0);
+      issue(b1, 1);
+      issue(b2, 2);
+    } else {
+      for (int t = 0; t < 3 && t < nbt; ++t) stage(t, t);
+    }
   }
 
   __device__ __forceinline__ void run(Buf& b0, Buf& b1, Buf& b2) const {
-    // Straight-line loop body (the compiler's wait counts stay exact across
-    // the back edge: consuming a buffer waits only for its own loads); the
-    // last one or two request tiles run after the loop.
-    int bt = 0;
-    for (; bt + 3 <= nbt; bt += 3) {
-      step(b0, bt);
-      step(b1, bt + 1);
-      step(b2, bt + 2);
+    if constexpr (CHECKED) {
+      // Straight-line loop body (the compiler's wait counts stay exact across
+      // the back edge: consuming a buffer waits only for its own loads); the
+      // last one or two request tiles run after the loop.
+      int bt = 0;
+      for (; bt + 3 <= nbt; bt += 3) {
+        step(b0, bt);
+        step(b1, bt + 1);
+        step(b2, bt + 2);
+      }
+      if (bt < nbt) step(b0, bt);
+      if (bt + 1 < nbt) step(b1, bt + 1);
+    } else {
+      int s = 0;
+      for (int bt = 0; bt < nbt; ++bt) {
+        f32x4_t acc[NTF];
+        unstage(s, min(2, nbt - 1 - bt), acc);
+        if (bt + 3 < nbt) stage(s, bt + 3);
+        tile(acc, bt);
+        s = (s == 2) ? 0 : s + 1;
+      }
     }
-    if (bt < nbt) step(b0, bt);
-    if (bt + 1 < nbt) step(b1, bt + 1);
+    lds_wait();   // this wave's key merges have landed
   }
 };
 
@@ -411,7 +481,8 @@ template <bool BF16, int R, int TPW, int GR, bool GUMBEL, int NTF, bool CHECKED>
 __device__ __forceinline__ TileWork<BF16, R, TPW, GR, GUMBEL, NTF, CHECKED> make_work(
     const typename Elem<BF16>::frag_t (&A)[TPW][R / Elem<BF16>::KS], const typename Elem<BF16>::store_t* lds_e,
     const typename Elem<BF16>::store_t* U, int g0, int rows, int B, int gamma, int k, int V, int w_lo, int nt,
-    int vec_ok, int li, int lg, uint32_t seed_lo, uint32_t seed_hi, uint64_t* lds_key, float* lds_zw) {
+    int vec_ok, int li, int lg, uint32_t seed_lo, uint32_t seed_hi, uint64_t* lds_key, float* lds_zw,
+    uint32_t* lds_u) {
   const size_t row_stride = size_t(gamma) * V;
   const int vlane = CHECKED ? w_lo * 16 + 4 * lg : w_lo * 16;
   const int oP0 = CHECKED ? 0 : pair_col(0, lg, nt, TPW);
@@ -419,10 +490,26 @@ __device__ __forceinline__ TileWork<BF16, R, TPW, GR, GUMBEL, NTF, CHECKED> make
   const int oL = CHECKED ? 0 : pair_col(TPW - 1, lg, nt, TPW);
   const int sw = ELayout<BF16, R>::swz(li);
   const int m = lg ^ (sw & 3), h = sw >> 2;
+  // staging slot: 16 rows of RS 16-byte chunks, the last chunk of a row and
+  // the positions past 16 rows being padding that receives a copy of chunk 0
+  const int RS = 2 * nt + 1;
+  const int lane = li + 16 * lg;
+  int dr[3], dc[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int pos = 64 * i + lane;
+    const int rr = pos / RS, cc = pos - rr * RS;
+    const bool real = rr < 16 && cc < 2 * nt;
+    dr[i] = real ? rr : 0;
+    dc[i] = real ? 8 * cc : 0;
+  }
+  const int rP0 = (li * RS + oP0 / 8) * 16, rP1 = (li * RS + oP1 / 8) * 16;
+  const int rL = (li * RS + oL / 8) * 16 + (oL & 7) * 2;
   return TileWork<BF16, R, TPW, GR, GUMBEL, NTF, CHECKED>{
       A, lds_e, lds_key, lds_zw, row_stride, U + (size_t(g0) * gamma + (k - 1)) * V + vlane,
       g0, rows, (rows + 15) >> 4, B, k, V, nt, vec_ok, li, lg, vlane, oP0, oP1, oL,
-      8 * (4 * h + m), 8 * (4 * (1 - h) + m), seed_lo, seed_hi};
+      8 * (4 * h + m), 8 * (4 * (1 - h) + m), lds_u, dr[0], dr[1], dr[2], dc[0], dc[1], dc[2],
+      rP0, rP1, rL, seed_lo, seed_hi};
 }
 
 // Hidden-state half of the confidence logit, hdot[b][k] = sum_j conf_w[j] *
@@ -497,6 +584,8 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   __shared__ double lds_hd[GR];
   __shared__ float lds_S[kMaxOwnedRows];
   __shared__ float lds_we[R];   // confidence weights of the Markov-embedding half
+  // U staging ring of the whole-tile path: three slots of 3 KB per wave
+  __shared__ __attribute__((aligned(16))) uint32_t lds_u[FULL ? NW * 3 * 768 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -635,7 +724,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   auto work = [&](int k, int g0, int rows) {
     return make_work<BF16, R, TPW, GR, GUMBEL, TPW, !FULL>(A, lds_e, U, g0, rows, B, gamma, k, V, w_lo, nt,
                                                            p.vec_ok, li, lg, p.seed_lo, p.seed_hi, lds_key,
-                                                           lds_z[wave]);
+                                                           lds_z[wave], lds_u + (FULL ? wave * 3 * 768 : 0));
   };
   auto bar = [&](int g) { return p.bar + size_t(g) * kBarStride; };
   typename Work::Buf pf0, pf1, pf2;
