@@ -28,13 +28,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-DRAFT_SOURCE = os.path.join(ROOT, "semi_ar_drafter_amd", "csrc", "markov_draft.hip")
+# the draft kernel's device code (the traffic summary is tied to these files)
+DRAFT_SOURCES = [os.path.join(ROOT, "semi_ar_drafter_amd", "csrc", f) for f in ("markov_draft.hip", "device_util.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "markov_draft_hbm_traffic.txt")
 
 
-def source_digest(path: str) -> str:
+def source_digest(paths) -> str:
     import hashlib
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -50,7 +54,7 @@ def measured_traffic():
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     try:
-        if vals.get("kernel_source_sha256") != source_digest(DRAFT_SOURCE):
+        if vals.get("kernel_source_sha256") != source_digest(DRAFT_SOURCES):
             return None
         fetch = float(vals["fetch_kib_per_launch"]) * 1024 * float(vals["fetch_scale"])
         write = float(vals["write_kib_per_launch"]) * 1024 * float(vals["write_scale"])
