@@ -54,8 +54,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
-    uint32_t hi0 = __umulhi(m0, c0), lo0 = m0 * c0;
-    uint32_t hi1 = __umulhi(m1, c2), lo1 = m1 * c2;
+    const uint64_t p0 = uint64_t(m0) * c0, p1 = uint64_t(m1) * c2;   // one 32x32->64 multiply each
+    const uint32_t hi0 = uint32_t(p0 >> 32), lo0 = uint32_t(p0);
+    const uint32_t hi1 = uint32_t(p1 >> 32), lo1 = uint32_t(p1);
     uint32_t n0 = hi1 ^ c1 ^ k0;
     uint32_t n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
@@ -66,9 +67,30 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
 
 // Standard Gumbel sample from one 32-bit hash word: u = (2*(w>>9)+1) * 2^-24
 // lies in (0, 1) and is exact in fp32; G = -ln(-ln u).
+//
+// Both logarithms use the hardware base-2 logarithm (v_log_f32, about 1 ulp
+// relative for normal arguments away from 1).  The inner one, L = -ln u, is
+// tiny when u is close to 1, where a hardware log2(u) would lose its relative
+// accuracy; there t = 1 - u (exact for u >= 1/2) is small and
+// L = -ln(1 - t) = t (1 + t/2 + t^2/3 + ... + t^6/7) is summed directly
+// (t <= 1/16: truncation below 5e-10 relative).  L >= 5.9e-8 is a normal
+// number, so the outer log2 is accurate too; the absolute error of G stays
+// around 1e-6.
 __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
-  float u = float((w >> 9) * 2u + 1u) * 0x1p-24f;
-  return -logf(-logf(u));
+  const uint32_t m2 = (w >> 9) * 2u + 1u;
+  const float u = float(m2) * 0x1p-24f;
+  const float t = 1.f - u;   // exact whenever it is used below (u >= 15/16)
+  const float ln2 = 0.693147180559945309f;
+  const float l_log = -__builtin_amdgcn_logf(u) * ln2;
+  float q = 1.f / 7.f;
+  q = q * t + 1.f / 6.f;
+  q = q * t + 0.2f;
+  q = q * t + 0.25f;
+  q = q * t + 1.f / 3.f;
+  q = q * t + 0.5f;
+  q = q * t + 1.f;
+  const float l = (t <= 0.0625f) ? q * t : l_log;
+  return -__builtin_amdgcn_logf(l) * ln2;
 }
 
 // 16-byte direct-to-LDS load (gfx950 global_load_lds_dwordx4): lane j of the
