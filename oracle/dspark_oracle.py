@@ -199,6 +199,49 @@ def draft(anchor, U, h, W1, W2, conf_w, conf_b, sts_T, sampling: str = "greedy",
 
 
 # ----------------------------------------------------------------------------
+# Parallel-only drafting (the baseline without a sequential head)
+# ----------------------------------------------------------------------------
+def parallel_draft(U, sampling: str = "greedy", seed: int = 0, rows=None):
+    """Drafting with the parallel stage alone: every position's token comes
+    from its own base logits, with no transition bias and no dependence on
+    the earlier draft tokens ([P-blog] §1 "Autoregressive vs Parallel
+    Drafting", the parallel drafters that emit logits for all positions in
+    one pass; §4 "Semi-Autoregressive Generation", parallel stage, U_k; §2
+    "Speedup formula": the sequential head is the lever on acceptance, paid
+    for in drafting time).
+
+    For each request b and k = 1..gamma: z_k = U_k (exact in fp32 for bf16 or
+    fp32 storage); x_k = the lowest vocabulary id with the largest score,
+    the score being z_k (greedy) or z_k + G(seed, b, k, v) in fp32, with the
+    same Gumbel noise as the Markov-head draft.  Reading: the baseline is the
+    Markov-head step with the transition bias removed, so the tokens are those
+    of draft() with W2 = 0; it drafts only (no confidence head).
+
+    Returns (tokens int32 [n, gamma], zsel fp32 [n, gamma]), zsel = z_k(x_k).
+    """
+    U = np.asarray(U)
+    B, gamma, V = U.shape
+    rows = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = rows.size
+    tokens = np.zeros((n, gamma), dtype=np.int32)
+    zsel = np.zeros((n, gamma), dtype=np.float32)
+    vv = np.arange(V, dtype=np.int64)
+    ar = np.arange(n)
+    for k in range(1, gamma + 1):
+        z = widen(U[rows, k - 1]).astype(np.float32)
+        if sampling == "greedy":
+            s = z
+        elif sampling == "gumbel":
+            s = z + gumbel_noise(seed, rows[:, None], k, vv[None, :])
+        else:
+            raise ValueError(sampling)
+        x = np.argmax(s, axis=1)                                 # first max
+        tokens[:, k - 1] = x
+        zsel[:, k - 1] = z[ar, x]
+    return tokens, zsel
+
+
+# ----------------------------------------------------------------------------
 # Hardware-aware prefix scheduler
 # ----------------------------------------------------------------------------
 def schedule(surv, t_step, n_min: int):
