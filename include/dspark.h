@@ -175,6 +175,38 @@ dspark_status dspark_verify(
     int B, int gamma, const int32_t* tokens, const int32_t* target, const int32_t* lens,
     int32_t* accepted, int32_t* bonus, hipStream_t stream);
 
+/*
+ * dspark_parallel_draft — drafting with the parallel stage alone: the
+ * baseline without a sequential head, for measuring what the Markov head
+ * adds to the drafting time.
+ *
+ * Defined by: [P-blog] §1 "Autoregressive vs Parallel Drafting" (parallel
+ * drafters emit the logits of every block position in one pass); §4
+ * "Semi-Autoregressive Generation", parallel stage (base logits U_k); §2
+ * "Speedup formula" (drafting time and acceptance as separate levers).
+ *
+ * For every request b and k = 1..gamma, independently:
+ *   x_k = smallest v maximising U[b][k-1][v]                 (GREEDY)
+ *       = smallest v maximising U[b][k-1][v] + G(seed,b,k,v)  (GUMBEL)
+ * with G the Gumbel noise of dspark_markov_draft (same generator, key and
+ * counter layout), i.e. the tokens dspark_markov_draft produces when W2 = 0.
+ *
+ * Arguments
+ *   B, gamma, V   requests, positions, vocabulary (B * gamma == 0 is a no-op)
+ *   dtype         storage of U (DSPARK_F32 or DSPARK_BF16)
+ *   U             [B][gamma][V]      base logits, element-aligned
+ *   mode, seed    sampling rule; seed used only for DSPARK_GUMBEL
+ *   tokens  int32 [B][gamma] out     x_k
+ *   logit   fp32  [B][gamma] out     U[b][k-1][x_k], without noise
+ * No workspace.  Rows are read with 16-byte loads when V is a multiple of
+ * 8 (bf16) or 4 (fp32) and U is 16-byte aligned, element by element
+ * otherwise.  Limits: V <= 2^24, B * gamma < 2^31.
+ */
+dspark_status dspark_parallel_draft(
+    int B, int gamma, int V, dspark_dtype dtype, const void* U,
+    dspark_sampling mode, uint64_t seed,
+    int32_t* tokens, float* logit, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* dspark_status_string(dspark_status s);
 

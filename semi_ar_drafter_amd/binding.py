@@ -43,6 +43,8 @@ def _declare(lib):
     lib.dspark_markov_draft.restype = c_int
     lib.dspark_schedule.argtypes = [c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
     lib.dspark_schedule.restype = c_int
+    lib.dspark_parallel_draft.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_int, c_u64, c_vp, c_vp, c_vp]
+    lib.dspark_parallel_draft.restype = c_int
     lib.dspark_verify.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
     lib.dspark_verify.restype = c_int
     lib.dspark_status_string.argtypes = [c_int]
@@ -164,6 +166,28 @@ def markov_draft(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, mode: str =
         _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
     _check(st)
     return tokens, logit, conf, surv
+
+
+def parallel_draft(U, mode: str = "greedy", seed: int = 0, out=None):
+    """Drafting without the sequential head: per position the arg-max of the
+    base logits (or of base logits + Gumbel noise).  U [B, gamma, V] float32
+    or bfloat16 device tensor; returns (tokens int32, logit fp32), [B, gamma]."""
+    torch = _torch()
+    lib = load()
+    _need(U, "U")
+    B, gamma, V = U.shape
+    dev = U.device
+    if U.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("U must be float32 or bfloat16")
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    tokens, logit = out
+    st = lib.dspark_parallel_draft(B, gamma, V, DSPARK_BF16 if U.dtype == torch.bfloat16 else DSPARK_F32, _ptr(U),
+                                   DSPARK_GUMBEL if mode == "gumbel" else DSPARK_GREEDY,
+                                   ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(tokens), _ptr(logit), _stream())
+    _check(st)
+    return tokens, logit
 
 
 def schedule(surv, t_step, n_min: int, out=None):

@@ -25,6 +25,7 @@ SOURCES = [
     ("api.cpp", False),
     ("markov_draft.hip", True),
     ("schedule_verify.hip", True),
+    ("parallel_draft.hip", True),
 ]
 
 

@@ -126,6 +126,26 @@ dspark_status dspark_schedule(int B, int gamma, const float* surv, const double*
   return DSPARK_OK;
 }
 
+dspark_status dspark_parallel_draft(int B, int gamma, int V, dspark_dtype dtype, const void* U,
+                                    dspark_sampling mode, uint64_t seed, int32_t* tokens, float* logit,
+                                    hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || gamma < 0 || V < 0) return fail(DSPARK_ERR_INVALID_ARG, "negative size");
+  if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_INVALID_ARG, "unknown dtype");
+  if (mode != DSPARK_GREEDY && mode != DSPARK_GUMBEL) return fail(DSPARK_ERR_INVALID_ARG, "unknown sampling mode");
+  if (B == 0 || gamma == 0) return DSPARK_OK;
+  if (V < 1) return fail(DSPARK_ERR_INVALID_ARG, "V must be positive");
+  if (!U || !tokens || !logit) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  if (V > kMaxV) return fail(DSPARK_ERR_UNSUPPORTED, "V > 2^24");
+  if ((long long)B * gamma > 0x7FFFFFFFLL) return fail(DSPARK_ERR_UNSUPPORTED, "B * gamma > 2^31 - 1");
+  const int elem = dtype == DSPARK_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(U) % elem) return fail(DSPARK_ERR_INVALID_ARG, "misaligned U");
+  hipError_t e = dspark::launch_parallel_draft(B, gamma, V, dtype == DSPARK_BF16, U, mode == DSPARK_GUMBEL, seed,
+                                               tokens, logit, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return DSPARK_OK;
+}
+
 dspark_status dspark_verify(int B, int gamma, const int32_t* tokens, const int32_t* target, const int32_t* lens,
                             int32_t* accepted, int32_t* bonus, hipStream_t stream) {
   g_last_error[0] = '\0';

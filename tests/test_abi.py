@@ -113,6 +113,19 @@ def test_verify_validation(lib):
     assert v(B=0, tk=NULL, tg=NULL) == OK
 
 
+def test_parallel_draft_validation(lib):
+    pd = lambda B=2, g=3, V=100, dt=1, U=P, mode=0, tk=P, lo=P: lib.dspark_parallel_draft(
+        B, g, V, dt, U, mode, 0, tk, lo, NULL)
+    assert pd(B=-1) == 1 and pd(V=-5) == 1
+    assert pd(dt=7) == 1 and pd(mode=3) == 1
+    assert pd(B=0) == 0 and pd(g=0) == 0            # empty: no-op, nothing launched
+    assert pd(V=0) == 1
+    assert pd(U=NULL) == 1 and pd(tk=NULL) == 1 and pd(lo=NULL) == 1
+    assert pd(V=(1 << 24) + 1) == 2
+    assert pd(U=ctypes.c_void_p(0x1001)) == 1       # bf16 element misaligned
+    assert lib.dspark_last_error().decode() != ""
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert lib.dspark_status_string(s).decode()
