@@ -13,7 +13,9 @@ n in [256, 4352] (synthetic inputs from the seeded generator).
 Prints one JSON line.  `value` = drafted tokens per second of the whole step
 (B * gamma / step time).  `roofline` rates the draft kernel against HBM
 bandwidth with its algorithmic bytes; `cpu_baseline` times the CPU oracle on
-a bounded sample of requests of the same workload.
+a bounded sample of requests of the same workload; `ablation` times
+dspark_parallel_draft (drafting without the sequential head) on the same U,
+outside the timed step.
 """
 from __future__ import annotations
 
@@ -135,7 +137,7 @@ def main():
     import numpy as np
     import torch
 
-    from semi_ar_drafter_amd import markov_draft, schedule, verify
+    from semi_ar_drafter_amd import markov_draft, parallel_draft, schedule, verify
     from semi_ar_drafter_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -196,6 +198,21 @@ def main():
     draft_avg = sum(draft_ms) / K
     value = B * g / (ms_step / 1e3)
 
+    # Ablation, outside the timed step: drafting with the parallel stage alone
+    # (no sequential head) on the same U, to show what the Markov head costs.
+    p_out = (torch.empty((B, g), dtype=torch.int32, device="cuda"),
+             torch.empty((B, g), dtype=torch.float32, device="cuda"))
+    for _ in range(2):
+        parallel_draft(U, mode=mode, seed=seed, out=p_out)
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a, b in pev:
+        a.record()
+        parallel_draft(U, mode=mode, seed=seed, out=p_out)
+        b.record()
+    torch.cuda.synchronize()
+    par_us = sum(a.elapsed_time(b) for a, b in pev) / len(pev) * 1e3
+    u_bytes = B * g * cfg.V * (2 if cfg.dtype == "bf16" else 4)
+
     abytes = algorithmic_bytes(cfg)
     achieved = abytes / (draft_avg / 1e3) / 1e9
     tflops = flops(cfg) / (draft_avg / 1e3) / 1e12
@@ -227,6 +244,11 @@ def main():
         "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
+        "ablation": {"parallel_only_us": round(par_us, 2),
+                     "parallel_only_gbs": round(u_bytes / (par_us / 1e6) / 1e9, 1),
+                     "markov_head_marginal_us": round(draft_avg * 1e3 - par_us, 2),
+                     "note": "dspark_parallel_draft on the same U (no transition bias, no confidence), "
+                             "timed separately from the step"},
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, min(args.cpu_rows, B), args.cpu_seconds)
