@@ -1,4 +1,5 @@
-"""CPU oracle for the DSpark Markov-head draft, prefix scheduler and verify step.
+"""CPU oracle for the DSpark Markov-head draft, prefix scheduler and verify
+step, parallel-only drafting and the sequential-temperature fit.
 
 TEST INFRASTRUCTURE.  Only the tests, the package entry's smoke check and the
 benchmark's CPU-baseline leg may import this module.  The library never does:
@@ -311,6 +312,98 @@ def verify(tokens, target, lens):
         accepted[b] = a
         bonus[b] = target[b, a]
     return accepted, bonus
+
+
+# ----------------------------------------------------------------------------
+# Sequential temperature scaling: fitting the per-position temperatures
+# ----------------------------------------------------------------------------
+def ece_fixed(p, y, n_bins: int):
+    """Expected calibration error of predicted probabilities p against 0/1
+    labels y: the samples are split into n_bins equal-width bins of p, and
+    each bin contributes its share of the samples times the gap between its
+    mean label and its mean prediction ([P-blog] §5 "Sequential Temperature
+    Scaling" names ECE as the objective; the pages give no bin count or rule).
+
+    Since (n_m / N) |mean y - mean p| = |sum over the bin of (y - p)| / N,
+    ECE = sum_m |sum_{n in bin m} (y_n - p_n)| / N.  Readings: bin(p) =
+    min(floor(p * n_bins), n_bins - 1), so p = 1 falls in the last bin; each
+    residual y - p is rounded to a multiple of 2^-32 (ties to even) and the
+    bin sums are exact integers, so comparing two candidates is exact.  The
+    last axis of p (and y, broadcast) runs over samples.
+
+    Returns (E, ece): E = sum_m |sum rint((y - p) 2^32)| as int64 per leading
+    index, ece = E / (2^32 N), and 0 when there are no samples.
+
+    The bin sums are taken by a weighted histogram in fp64, exact here: every
+    residual is an integer of magnitude <= 2^32, so with N <= 2^20 samples
+    every partial sum is an integer below 2^53.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    y = np.broadcast_to(np.asarray(y, dtype=np.float64), p.shape)
+    N = p.shape[-1]
+    if N > 2 ** 20:
+        raise ValueError("ece_fixed: more than 2^20 samples")
+    lead = p.shape[:-1]
+    R = int(np.prod(lead, dtype=np.int64))
+    bins = np.minimum(np.floor(p * n_bins), n_bins - 1).astype(np.int64)
+    q = np.rint((y - p) * TWO32)                                 # integers, |q| <= 2^32
+    key = (np.arange(R, dtype=np.int64).reshape(lead + (1,)) * n_bins + bins).ravel()
+    sums = np.bincount(key, weights=q.ravel(), minlength=R * n_bins).reshape(R, n_bins)
+    E = np.abs(sums.astype(np.int64)).sum(axis=1).reshape(lead)
+    ece = E / (TWO32 * N) if N > 0 else np.zeros(E.shape, dtype=np.float64)
+    return E, ece
+
+
+def sts_fit(logit, accepted, grid, n_bins: int, choose: Optional[Callable] = None,
+            g_chunk: int = 16):
+    """Sequential temperature scaling fitted left to right ([P-blog] §5
+    "Sequential Temperature Scaling"; [P-wisp] "Critical Insights"; [P-news]
+    on post-hoc calibration against empirical acceptance).
+
+    logit[n][k-1] is block n's raw confidence logit at draft position k (the
+    pre-sigmoid value of the confidence head, bias included, read as fp32);
+    accepted[n] is how many leading drafts of block n the target accepted.
+    For k = 1..gamma, in order:
+      * y_n = 1 when accepted[n] >= k: the survival label, since the
+        calibrated quantity is the cumulative product S_k, the probability
+        that drafts 1..k are all accepted (reading);
+      * for every candidate T of the grid, p_n(T) = S_{n,k-1} sigmoid(logit
+        / T), the earlier positions held at their fitted temperatures
+        (S_{n,0} = 1; T divides the whole logit, as in the draft step);
+      * T_k = the candidate with the smallest ECE of p(T) against y (a 1-D
+        grid search); among equal ECE the first in grid order (reading);
+      * S_{n,k} = p_n(T_k).
+    fp64 throughout; the comparison uses ece_fixed's exact integer sums.
+
+    `choose(k, E, g)` may replace the chosen grid index at position k (E: the
+    integer objective per candidate, g: the oracle's choice); the fit goes on
+    from whatever it returns.
+
+    Returns (choice int32 [gamma], T fp32 [gamma], ece fp64 [gamma][G]).
+    """
+    L = widen(np.asarray(logit, dtype=np.float32))
+    N, gamma = L.shape
+    T_grid = np.asarray(grid, dtype=np.float32)
+    Tg = T_grid.astype(np.float64)
+    G = Tg.size
+    a = np.asarray(accepted, dtype=np.int64)
+    S = np.ones(N, dtype=np.float64)
+    choice = np.zeros(gamma, dtype=np.int32)
+    T_out = np.zeros(gamma, dtype=np.float32)
+    ece = np.zeros((gamma, G), dtype=np.float64)
+    for k in range(1, gamma + 1):
+        y = (a >= k).astype(np.float64)
+        E = np.zeros(G, dtype=np.int64)
+        for g0 in range(0, G, g_chunk):                         # bounds host memory
+            P = S[None, :] * sigmoid64(L[:, k - 1][None, :] / Tg[g0:g0 + g_chunk, None])
+            E[g0:g0 + g_chunk], ece[k - 1, g0:g0 + g_chunk] = ece_fixed(P, y, n_bins)
+        g = int(np.argmin(E))                                   # first minimum
+        if choose is not None:
+            g = int(choose(k, E, g))
+        choice[k - 1] = g
+        T_out[k - 1] = T_grid[g]
+        S = S * sigmoid64(L[:, k - 1] / Tg[g])
+    return choice, T_out, ece
 
 
 def draft_workload(w: dict, rows=None, choose=None, trace=None, seed=None):

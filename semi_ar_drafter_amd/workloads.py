@@ -55,6 +55,7 @@ SEED_ROOT = 20260629
 # Fixed per-tensor stream tags (never reorder: they define the bytes).
 _TAG_W1, _TAG_W2, _TAG_CONFW = 1, 2, 3
 _TAG_ANCHOR, _TAG_U, _TAG_PLANT, _TAG_H, _TAG_TGT_COIN, _TAG_TGT_UNI = 10, 11, 12, 13, 14, 15
+_TAG_STS_LOGIT, _TAG_STS_NOISE = 20, 21
 
 
 @dataclasses.dataclass(frozen=True)
@@ -200,3 +201,52 @@ def small_config(B: int, gamma: int, V: int, r: int, d: int, dtype: str = "bf16"
     several tiles and ragged tails at sizes the oracle finishes quickly)."""
     return Config(cid, f"custom-{B}x{gamma}x{V}x{r}x{d}-{dtype}", B, gamma, V, r, d, dtype,
                   plant, p_target, sps, sampling=sampling)
+
+
+# ----------------------------------------------------------------------------
+# Calibration sets for fitting the sequential temperatures
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class STSConfig:
+    cid: int
+    name: str
+    N: int                      # calibration blocks
+    gamma: int                  # draft positions per block
+    G: int                      # candidate temperatures (geometric grid)
+    n_bins: int                 # calibration-error bins
+    mu: tuple = (3.5, 1.0)      # mean raw confidence logit at k = 1 and k = gamma
+    sd: float = 2.0             # its standard deviation
+    t_true: tuple = (1.4, 2.6)  # temperature of the acceptance process, k = 1 and k = gamma
+    grid: tuple = (0.25, 8.0)   # first and last candidate temperature
+
+    def replace(self, **kw) -> "STSConfig":
+        return dataclasses.replace(self, **kw)
+
+
+STS_CONFIGS = {
+    0: STSConfig(200, "sts-small", 3000, 4, 24, 15),
+    1: STSConfig(201, "sts-calibration-256k", 262144, 16, 128, 15),
+}
+
+
+def make_sts_calibration(cfg: STSConfig) -> dict:
+    """Synthetic calibration set: raw confidence logits and accepted lengths.
+
+    logit[n][k-1] ~ N(mu_k, sd^2) in fp32 (mu linear in k).  Acceptance is a
+    strict prefix process: draft k of block n is accepted, given drafts
+    1..k-1 were, when logit/t_true_k + L > 0 for a standard logistic L, i.e.
+    with probability sigmoid(logit / t_true_k); accepted[n] counts the leading
+    accepted drafts.  t_true > 1 makes the raw scores overconfident.  The
+    candidate temperatures are a geometric fp32 grid.
+    """
+    N, g = cfg.N, cfg.gamma
+    mu = linear_in_k(cfg.mu[0], cfg.mu[1], g).astype(np.float32)
+    t_true = linear_in_k(cfg.t_true[0], cfg.t_true[1], g)
+    logit = (_rng(cfg, _TAG_STS_LOGIT).standard_normal((N, g), dtype=np.float32) * np.float32(cfg.sd)
+             + mu[None, :]).astype(np.float32)
+    noise = _rng(cfg, _TAG_STS_NOISE).logistic(size=(N, g))
+    ok = logit.astype(np.float64) / t_true[None, :] + noise > 0.0
+    accepted = np.cumprod(ok, axis=1).sum(axis=1).astype(np.int32)
+    grid = np.geomspace(cfg.grid[0], cfg.grid[1], cfg.G).astype(np.float32)
+    return dict(logit=np.ascontiguousarray(logit), accepted=accepted, grid=grid,
+                n_bins=cfg.n_bins, t_true=t_true, cfg=cfg)

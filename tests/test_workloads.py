@@ -46,3 +46,19 @@ def test_plants_and_targets():
     assert got[:, 0].mean() > 7.5 and got[:, -1].mean() < 6.0      # 9 -> 5 decay
     agree = (w["target"][:, :16] == w["plant"]).mean(axis=0)
     assert agree[0] > 0.8 and agree[-1] < 0.8
+
+
+def test_sts_calibration_set_is_deterministic_and_well_formed():
+    cfg = wl.STS_CONFIGS[0]
+    a = wl.make_sts_calibration(cfg)
+    b = wl.make_sts_calibration(cfg)
+    for key in ("logit", "accepted", "grid"):
+        assert np.array_equal(a[key], b[key])
+    assert a["logit"].shape == (cfg.N, cfg.gamma) and a["logit"].dtype == np.float32
+    assert a["accepted"].dtype == np.int32
+    assert a["accepted"].min() >= 0 and a["accepted"].max() <= cfg.gamma
+    assert a["grid"].shape == (cfg.G,) and np.all(np.diff(a["grid"]) > 0)
+    assert a["grid"][0] == np.float32(cfg.grid[0])
+    # a different config id gives a different set
+    c = wl.make_sts_calibration(cfg.replace(cid=cfg.cid + 1))
+    assert not np.array_equal(a["logit"], c["logit"])
