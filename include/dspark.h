@@ -207,6 +207,54 @@ dspark_status dspark_parallel_draft(
     dspark_sampling mode, uint64_t seed,
     int32_t* tokens, float* logit, hipStream_t stream);
 
+/*
+ * dspark_sts_fit — fits the confidence head's per-position temperatures
+ * T_1..T_gamma, left to right, on a calibration set.
+ *
+ * Defined by: [P-blog] §5 "Sequential Temperature Scaling" (raw confidence
+ * is overconfident; the joint probability is calibrated position by
+ * position, each by a 1-D grid search for the temperature minimising the
+ * expected calibration error of the cumulative product, earlier positions
+ * held at their calibrated values); [P-wisp] "Critical Insights"
+ * (calibration is required for the scheduler); [P-news] (calibration
+ * against empirical acceptance).
+ *
+ * For k = 1..gamma, in order, with S_{n,0} = 1 and y_n = (accepted[n] >= k):
+ *   p_n(T)  = S_{n,k-1} * sigmoid(logit[n][k-1] / T)       for every T in grid
+ *   ECE(T)  = sum_m |sum_{n: bin(p_n) = m} rint((y_n - p_n) 2^32)| / (2^32 N),
+ *             bin(p) = min(floor(p * n_bins), n_bins - 1)
+ *   T_k     = the first grid entry with the smallest ECE (compared exactly,
+ *             on the integer sums)
+ *   S_{n,k} = p_n(T_k)
+ * in fp64.  The result is independent of thread and workgroup order.
+ *
+ * Arguments
+ *   N             calibration blocks (0 allowed: every ECE is 0, T_k = grid[0])
+ *   gamma         positions (0: no-op)
+ *   logit  fp32  [N][gamma]  raw confidence logits (pre-sigmoid, bias included, T = 1)
+ *   accepted int32 [N]       accepted drafts per block; values above gamma act
+ *                            as gamma, negative ones as 0
+ *   grid   fp32  [G]         candidate temperatures, positive and finite
+ *   n_bins                   calibration-error bins over [0, 1]
+ *   choice int32 [gamma] out grid index of T_k
+ *   T_out  fp32  [gamma] out T_k (ready to pass as sts_T to dspark_markov_draft)
+ *   ece    fp64  [gamma][G] out the ECE of every candidate at every position
+ *   workspace     device memory of dspark_sts_workspace_bytes(N, G, n_bins)
+ *                 bytes, 256-byte aligned, any contents (the call clears what
+ *                 it needs).  Calls sharing a workspace must not overlap.
+ * All arrays are device memory owned by the caller.  Limits: G <= 4096,
+ * n_bins <= 256, G * n_bins <= 8192, N <= 2^24, N * gamma < 2^31, else
+ * DSPARK_ERR_UNSUPPORTED.  Non-positive or non-finite temperatures and
+ * non-finite logits are outside the contract (results unspecified; memory
+ * accesses stay in bounds).  Runs gamma + 1 kernel launches on `stream`.
+ */
+size_t dspark_sts_workspace_bytes(int N, int G, int n_bins);
+
+dspark_status dspark_sts_fit(
+    int N, int gamma, const float* logit, const int32_t* accepted, const float* grid,
+    int G, int n_bins, int32_t* choice, float* T_out, double* ece,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* dspark_status_string(dspark_status s);
 

@@ -45,6 +45,11 @@ def _declare(lib):
     lib.dspark_schedule.restype = c_int
     lib.dspark_parallel_draft.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_int, c_u64, c_vp, c_vp, c_vp]
     lib.dspark_parallel_draft.restype = c_int
+    lib.dspark_sts_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    lib.dspark_sts_workspace_bytes.restype = c_size
+    lib.dspark_sts_fit.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
+                                   c_size, c_vp]
+    lib.dspark_sts_fit.restype = c_int
     lib.dspark_verify.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
     lib.dspark_verify.restype = c_int
     lib.dspark_status_string.argtypes = [c_int]
@@ -114,9 +119,9 @@ def workspace_bytes(B: int, gamma: int, V: int, r: int) -> int:
     return int(load().dspark_draft_workspace_bytes(B, gamma, V, r))
 
 
-def _workspace(nbytes: int, device):
+def _workspace(nbytes: int, device, kind: str = "draft"):
     torch = _torch()
-    key = (device.index if device.index is not None else torch.cuda.current_device())
+    key = (kind, device.index if device.index is not None else torch.cuda.current_device())
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         # zero-filled once; every completed call leaves it zero-filled again
@@ -188,6 +193,32 @@ def parallel_draft(U, mode: str = "greedy", seed: int = 0, out=None):
                                    ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(tokens), _ptr(logit), _stream())
     _check(st)
     return tokens, logit
+
+
+def sts_fit(logit, accepted, grid, n_bins: int, out=None, workspace=None):
+    """Fit the per-position confidence temperatures on a calibration set:
+    logit fp32 [N, gamma] raw confidence logits, accepted int32 [N], grid
+    fp32 [G] candidate temperatures.  Returns (choice int32 [gamma], T fp32
+    [gamma], ece fp64 [gamma, G])."""
+    torch = _torch()
+    lib = load()
+    _need(logit, "logit", torch.float32)
+    N, gamma = logit.shape
+    dev = logit.device
+    _need(accepted, "accepted", torch.int32, (N,), dev)
+    _need(grid, "grid", torch.float32, None, dev)
+    G = grid.numel()
+    if out is None:
+        out = (torch.empty(gamma, dtype=torch.int32, device=dev),
+               torch.empty(gamma, dtype=torch.float32, device=dev),
+               torch.empty((gamma, G), dtype=torch.float64, device=dev))
+    choice, T, ece = out
+    nbytes = int(lib.dspark_sts_workspace_bytes(N, G, n_bins))
+    ws = workspace if workspace is not None else _workspace(nbytes, dev, "sts")
+    st = lib.dspark_sts_fit(N, gamma, _ptr(logit), _ptr(accepted), _ptr(grid), G, int(n_bins),
+                            _ptr(choice), _ptr(T), _ptr(ece), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    _check(st)
+    return choice, T, ece
 
 
 def schedule(surv, t_step, n_min: int, out=None):

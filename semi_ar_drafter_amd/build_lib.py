@@ -26,6 +26,7 @@ SOURCES = [
     ("markov_draft.hip", True),
     ("schedule_verify.hip", True),
     ("parallel_draft.hip", True),
+    ("sts_fit.hip", True),
 ]
 
 

@@ -146,6 +146,49 @@ dspark_status dspark_parallel_draft(int B, int gamma, int V, dspark_dtype dtype,
   return DSPARK_OK;
 }
 
+size_t dspark_sts_workspace_bytes(int N, int G, int n_bins) {
+  if (N < 0 || G < 1 || n_bins < 1 || G > dspark::kMaxStsGrid || n_bins > dspark::kMaxStsBins) return 0;
+  return dspark::sts_workspace_layout(N, G, n_bins).total;
+}
+
+dspark_status dspark_sts_fit(int N, int gamma, const float* logit, const int32_t* accepted, const float* grid,
+                             int G, int n_bins, int32_t* choice, float* T_out, double* ece, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || gamma < 0 || G < 0 || n_bins < 0) return fail(DSPARK_ERR_INVALID_ARG, "negative size");
+  if (gamma == 0) return DSPARK_OK;
+  if (G < 1 || n_bins < 1) return fail(DSPARK_ERR_INVALID_ARG, "G and n_bins must be positive");
+  if (!grid || !choice || !T_out || !ece || (N > 0 && (!logit || !accepted)))
+    return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  if (G > dspark::kMaxStsGrid) return fail(DSPARK_ERR_UNSUPPORTED, "G > 4096");
+  if (n_bins > dspark::kMaxStsBins) return fail(DSPARK_ERR_UNSUPPORTED, "n_bins > 256");
+  if ((long long)G * n_bins > dspark::kMaxStsHist) return fail(DSPARK_ERR_UNSUPPORTED, "G * n_bins > 8192");
+  if (N > dspark::kMaxStsBlocks) return fail(DSPARK_ERR_UNSUPPORTED, "N > 2^24");
+  if ((long long)N * gamma > 0x7FFFFFFFLL) return fail(DSPARK_ERR_UNSUPPORTED, "N * gamma > 2^31 - 1");
+  if (reinterpret_cast<uintptr_t>(logit) % 4 || reinterpret_cast<uintptr_t>(accepted) % 4 ||
+      reinterpret_cast<uintptr_t>(grid) % 4 || reinterpret_cast<uintptr_t>(ece) % 8)
+    return fail(DSPARK_ERR_INVALID_ARG, "misaligned tensor");
+  const size_t need = dspark_sts_workspace_bytes(N, G, n_bins);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSPARK_ERR_WORKSPACE, "workspace missing or smaller than dspark_sts_workspace_bytes()");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(DSPARK_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  dspark::StsArgs a;
+  a.N = N;
+  a.gamma = gamma;
+  a.G = G;
+  a.nbins = n_bins;
+  a.logit = logit;
+  a.accepted = accepted;
+  a.grid = grid;
+  a.choice = choice;
+  a.T_out = T_out;
+  a.ece = ece;
+  a.ws = workspace;
+  hipError_t e = dspark::launch_sts_fit(a, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return DSPARK_OK;
+}
+
 dspark_status dspark_verify(int B, int gamma, const int32_t* tokens, const int32_t* target, const int32_t* lens,
                             int32_t* accepted, int32_t* bonus, hipStream_t stream) {
   g_last_error[0] = '\0';

@@ -51,6 +51,31 @@ hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_
 hipError_t launch_parallel_draft(int B, int gamma, int V, bool bf16, const void* U, bool gumbel, uint64_t seed,
                                  int32_t* tokens, float* logit, hipStream_t stream);
 
+// Sequential-temperature fit: limits of one workgroup's LDS histogram.
+constexpr int kMaxStsGrid = 4096;
+constexpr int kMaxStsBins = 256;
+constexpr int kMaxStsHist = 8192;     // nbins * G
+constexpr int kMaxStsBlocks = 1 << 24;
+
+struct StsArgs {
+  int N, gamma, G, nbins;
+  const float* logit;
+  const int32_t* accepted;
+  const float* grid;
+  int32_t* choice;
+  float* T_out;
+  double* ece;
+  void* ws;
+};
+
+struct StsWorkspace {
+  size_t ctrl, hist, S, total;
+};
+StsWorkspace sts_workspace_layout(int N, int G, int nbins);
+size_t sts_lds_bytes(int G, int nbins);
+
+hipError_t launch_sts_fit(const StsArgs& a, hipStream_t stream);
+
 hipError_t launch_verify(int B, int gamma, const int32_t* tokens, const int32_t* target,
                          const int32_t* lens, int32_t* accepted, int32_t* bonus, hipStream_t stream);
 

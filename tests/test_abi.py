@@ -126,6 +126,34 @@ def test_parallel_draft_validation(lib):
     assert lib.dspark_last_error().decode() != ""
 
 
+def test_sts_fit_validation(lib):
+    ws_need = lib.dspark_sts_workspace_bytes(1000, 24, 15)
+    assert ws_need >= 256 + 24 * 15 * 8 + 1000 * 8
+    assert lib.dspark_sts_workspace_bytes(-1, 24, 15) == 0 and lib.dspark_sts_workspace_bytes(10, 0, 15) == 0
+    assert lib.dspark_sts_workspace_bytes(10, 4097, 1) == 0 and lib.dspark_sts_workspace_bytes(10, 2, 257) == 0
+
+    def fit(N=1000, g=4, lo=P, acc=P, grid=P, G=24, M=15, ch=P, T=P, ece=P, ws=P, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = ws_need
+        return lib.dspark_sts_fit(N, g, lo, acc, grid, G, M, ch, T, ece, ws, ctypes.c_size_t(ws_bytes), NULL)
+
+    assert fit(N=-1) == INVALID and fit(g=-2) == INVALID and fit(G=-1) == INVALID and fit(M=-3) == INVALID
+    assert fit(g=0) == OK                                   # no-op, nothing launched
+    assert fit(G=0) == INVALID and fit(M=0) == INVALID
+    for k in ("lo", "acc", "grid", "ch", "T", "ece"):
+        assert fit(**{k: NULL}) == INVALID, k
+    assert fit(G=4097, ws_bytes=1 << 30) == UNSUPPORTED
+    assert fit(M=257, G=2, ws_bytes=1 << 30) == UNSUPPORTED
+    assert fit(G=1024, M=9, ws_bytes=1 << 30) == UNSUPPORTED   # histogram over 8192 entries
+    assert fit(N=(1 << 24) + 1, ws_bytes=1 << 40) == UNSUPPORTED
+    assert fit(N=1 << 24, g=200, ws_bytes=1 << 40) == UNSUPPORTED   # N * gamma >= 2^31
+    assert fit(lo=ctypes.c_void_p(0x10002)) == INVALID
+    assert fit(ece=ctypes.c_void_p(0x10004)) == INVALID
+    assert fit(ws=NULL) == WORKSPACE and fit(ws_bytes=ws_need - 1) == WORKSPACE
+    assert fit(ws=ctypes.c_void_p(0x10080)) == WORKSPACE
+    assert "workspace" in lib.dspark_last_error().decode()
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert lib.dspark_status_string(s).decode()
