@@ -15,7 +15,9 @@ Prints one JSON line.  `value` = drafted tokens per second of the whole step
 bandwidth with its algorithmic bytes; `cpu_baseline` times the CPU oracle on
 a bounded sample of requests of the same workload; `ablation` times
 dspark_parallel_draft (drafting without the sequential head) on the same U,
-outside the timed step.
+outside the timed step; `sts_fit` times dspark_sts_fit (fitting the 16
+confidence temperatures on 262144 synthetic calibration blocks, 128 candidate
+temperatures, 15 bins), also outside the step, against the VALU issue rate.
 """
 from __future__ import annotations
 
@@ -29,6 +31,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes per cycle x 2.4 GHz (one fp64
+# or fp32 vector op per lane per cycle; 78.6 TFLOP/s fp64 counts an FMA as 2)
+VALU_PEAK_GOPS = 256 * 64 * 2.4
+# Operations one candidate evaluation of the temperature fit needs: scale by
+# 1/T (1); e^x: range reduction (4), degree-13 polynomial (13), scaling (1);
+# 1 + e^x (1); reciprocal estimate + two Newton steps (5); p = S sigmoid (1);
+# y - p (1); rounding to 2^-32 (2); bin index (3); histogram address (1);
+# histogram add (1).
+STS_OPS_PER_EVAL = 34
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # the draft kernel's device code (the traffic summary is tied to these files)
 DRAFT_SOURCES = [os.path.join(ROOT, "semi_ar_drafter_amd", "csrc", f) for f in ("markov_draft.hip", "device_util.h")]
@@ -116,6 +127,34 @@ def cpu_baseline(w, rows: int, min_seconds: float):
     return dict(seconds=t1 - t0, tokens=reps * rows * w["cfg"].gamma, threads=threads, reps=reps)
 
 
+def time_sts_fit(torch, wl, sts_fit, reps: int = 10):
+    """Times dspark_sts_fit on the 262144-block calibration set (inputs in HBM)."""
+    c = wl.STS_CONFIGS[1]
+    cal = wl.make_sts_calibration(c)
+    lo = torch.from_numpy(cal["logit"]).cuda()
+    ac = torch.from_numpy(cal["accepted"]).cuda()
+    gr = torch.from_numpy(cal["grid"]).cuda()
+    out = (torch.empty(c.gamma, dtype=torch.int32, device="cuda"),
+           torch.empty(c.gamma, dtype=torch.float32, device="cuda"),
+           torch.empty((c.gamma, c.G), dtype=torch.float64, device="cuda"))
+    for _ in range(2):
+        sts_fit(lo, ac, gr, c.n_bins, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        sts_fit(lo, ac, gr, c.n_bins, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)[reps // 2]
+    evals = c.N * c.gamma * c.G
+    gops = evals * STS_OPS_PER_EVAL / (us / 1e6) / 1e9
+    return {"workload": f"calibration N={c.N} gamma={c.gamma} G={c.G} bins={c.n_bins}",
+            "us_per_fit": round(us, 1), "evals_per_s": round(evals / (us / 1e6), 1),
+            "roofline": {"bound": "alu", "achieved": round(gops, 1), "peak": VALU_PEAK_GOPS, "unit": "Gop/s",
+                         "frac": round(gops / VALU_PEAK_GOPS, 4), "ops_per_eval": STS_OPS_PER_EVAL,
+                         "kernel": f"sts_pass_kernel ({c.gamma} launches + 1 clear per fit)"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +164,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=256, help="requests in the CPU-oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sts", action="store_true", help="skip timing the temperature fit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (for HBM counter scaling) and exit")
     args = ap.parse_args()
@@ -137,7 +177,7 @@ def main():
     import numpy as np
     import torch
 
-    from semi_ar_drafter_amd import markov_draft, parallel_draft, schedule, verify
+    from semi_ar_drafter_amd import markov_draft, parallel_draft, schedule, sts_fit, verify
     from semi_ar_drafter_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -250,6 +290,8 @@ def main():
                      "note": "dspark_parallel_draft on the same U (no transition bias, no confidence), "
                              "timed separately from the step"},
     }
+    if not args.no_sts:
+        result["sts_fit"] = time_sts_fit(torch, wl, sts_fit)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, min(args.cpu_rows, B), args.cpu_seconds)
         result["cpu_baseline"] = {"value": round(cb["tokens"] / cb["seconds"], 2), "unit": "drafted tokens/s",

@@ -6,15 +6,16 @@
 // speculative decoding work", §5 "Sequential Temperature Scaling").
 //
 // One launch per position.  A launch splits the calibration blocks into
-// chunks, one workgroup per compute unit; within a workgroup every lane owns
-// one candidate temperature, so all 64 lanes of a wave read the same staged
-// block (an LDS broadcast) and update different histogram entries.  For block
-// n and candidate g:
+// rounds of staged blocks, several workgroups per compute unit; within a
+// workgroup the lanes of a wave hold different candidate temperatures and
+// read the same staged block (an LDS broadcast).  For block n and candidate g:
 //     p = S_{n,k-1} * sigmoid(logit[n][k-1] / T_g)          (fp64)
 //     bin = min(floor(p * nbins), nbins - 1)
 //     hist[bin][g] += rint((y_n - p) * 2^32)                 (exact int64)
-// with y_n = (accepted[n] >= k).  The workgroup's histogram lives in LDS and
-// is added to the device histogram with 64-bit atomics; the last workgroup to
+// with y_n = (accepted[n] >= k).  The workgroup keeps one LDS column of bins
+// per candidate and adds to it with 64-bit LDS atomics (for G >= 128 the 64
+// lanes of a wave hold 64 different candidates); workgroup histograms are
+// added to the device histogram with 64-bit atomics; the last workgroup to
 // arrive turns the device histogram into ECE_g = sum_bin |hist| / (2^32 N),
 // picks the first g with the smallest integer sum, and clears the histogram
 // and the arrival counter for the next launch (a small kernel clears them
@@ -30,8 +31,6 @@
 namespace dspark {
 namespace {
 
-constexpr int kStsThreads = 1024;   // threads per workgroup = blocks staged per round
-
 struct StsParams {
   const float* logit;          // [N][gamma] raw confidence logits
   const int32_t* accepted;     // [N] accepted drafts per block
@@ -46,25 +45,85 @@ struct StsParams {
   double* S;                   // [N] prefix products of the fitted positions
 };
 
-// sigmoid(l / T) with l / T taken as l * (1 / T), in the order the fit uses
-// everywhere (no contraction, so the prefix product carried to the next
-// position equals the value scored here).
-__device__ __forceinline__ double sigmoid_scaled(double l, double inv_t) {
-#pragma clang fp contract(off)
-  const double x = l * inv_t;
-  return 1.0 / (1.0 + exp(-x));
+constexpr double kMagic = 6755399441055744.0;   // 1.5 * 2^52: x + kMagic rounds x to an integer
+
+// q * r + c with the coefficient c in scalar registers: a three-operand fma
+// that leaves every vector register of the chain in place (the compiler
+// otherwise copies the coefficient into the accumulator of a two-operand fma).
+__device__ __forceinline__ double horner_step(double q, double r, double c) {
+  double out;
+  asm("v_fma_f64 %0, %1, %2, %3" : "=v"(out) : "v"(q), "v"(r), "s"(c));
+  return out;
 }
 
-// rint(v) as an int64 for |v| < 2^51: adding 1.5 * 2^52 leaves the integer
-// nearest to v (ties to even, the default rounding) in the low mantissa bits.
-__device__ __forceinline__ long long rint_to_i64(double v) {
+// e^x for x in [-745, 708] (the caller clamps), about 2 ulp.  x = n ln2 + r
+// with n = rint(x / ln2), read from the low word of x log2(e) + 1.5 * 2^52,
+// and r = x - n ln2 in two steps (ln2 split into a 32-bit head, so n times
+// the head is exact, and a tail); |r| <= ln2 / 2, where the Taylor series of
+// e^r to degree 13 is within 2^-54 relative; the result is scaled by 2^n.
+__device__ __forceinline__ double exp_clamped(double x) {
+  constexpr double kLog2e = 1.4426950408889634;
+  constexpr double kLn2Hi = 6.93147180369123816490e-01;   // 0x3FE62E42FEE00000
+  constexpr double kLn2Lo = 1.90821492927058770002e-10;   // ln2 - kLn2Hi
+  const double t = __builtin_fma(x, kLog2e, kMagic);
+  const int n = static_cast<int>(static_cast<uint32_t>(__double_as_longlong(t)));
+  const double nf = t - kMagic;
+  double r = __builtin_fma(-nf, kLn2Hi, x);
+  r = __builtin_fma(-nf, kLn2Lo, r);
+  double q = horner_step(1.0 / 6227020800.0, r, 1.0 / 479001600.0);   // 1/13!, 1/12!
+  q = horner_step(q, r, 1.0 / 39916800.0);
+  q = horner_step(q, r, 1.0 / 3628800.0);
+  q = horner_step(q, r, 1.0 / 362880.0);
+  q = horner_step(q, r, 1.0 / 40320.0);
+  q = horner_step(q, r, 1.0 / 5040.0);
+  q = horner_step(q, r, 1.0 / 720.0);
+  q = horner_step(q, r, 1.0 / 120.0);
+  q = horner_step(q, r, 1.0 / 24.0);
+  q = horner_step(q, r, 1.0 / 6.0);
+  q = __builtin_fma(q, r, 0.5);
+  q = __builtin_fma(q, r, 1.0);
+  q = __builtin_fma(q, r, 1.0);
+  return ldexp(q, n);
+}
+
+// sigmoid(l / T) = 1 / (1 + e^{l * (-1/T)}), the argument clamped to the range
+// where e^x is finite (1 + e^x then stays finite; beyond it the sigmoid is 0
+// or 1 to within 1e-300).  The reciprocal is the hardware estimate refined by
+// two Newton steps.  Scoring and the prefix product carried to the next
+// position both come from here, so they agree bit for bit.
+__device__ __forceinline__ double sigmoid_scaled(double l, double neg_inv_t) {
+  const double x = fmin(fmax(l * neg_inv_t, -745.0), 708.0);
+  const double a = 1.0 + exp_clamped(x);
+  double r = __builtin_amdgcn_rcp(a);
+  r = __builtin_fma(r, __builtin_fma(-a, r, 1.0), r);
+  r = __builtin_fma(r, __builtin_fma(-a, r, 1.0), r);
+  return r;
+}
+
+// One candidate's contribution for one staged block: the bin of
+// p = S * sigmoid(l / T) and rint((y - p) * 2^32).  p and y - p are rounded
+// separately (no contraction); the product by 2^32 is exact, so
+// fma(y - p, 2^32, 1.5 * 2^52) rounds once, to the nearest integer (ties to
+// even), which sits in the low mantissa bits.
+struct Scored {
+  unsigned int bin;
+  unsigned long long q;   // two's-complement int64
+};
+__device__ __forceinline__ Scored score(double l, double S, double y, double neg_inv_t, int nbins) {
 #pragma clang fp contract(off)
-  constexpr double kMagic = 6755399441055744.0;   // 1.5 * 2^52
-  return __double_as_longlong(v + kMagic) - __double_as_longlong(kMagic);
+  const double pr = S * sigmoid_scaled(l, neg_inv_t);
+  const double biased = __builtin_fma(y - pr, 4294967296.0, kMagic);
+  Scored r;
+  r.q = static_cast<unsigned long long>(__double_as_longlong(biased) - __double_as_longlong(kMagic));
+  const unsigned int b = static_cast<unsigned int>(pr * double(nbins));   // pr >= 0; NaN -> 0
+  r.bin = min(b, unsigned(nbins - 1));
+  return r;
 }
 
 // Histogram bytes rounded up to 16 (the staged pairs that follow are 16-byte loads).
 __host__ __device__ constexpr size_t sts_hist_lds_bytes(int nh) { return (size_t(nh) * 8 + 15) & ~size_t(15); }
+
+constexpr int kStsThreads = 1024;   // threads per workgroup = blocks staged per round
 
 __global__ void __launch_bounds__(kStsThreads) sts_clear_kernel(unsigned int* done, unsigned long long* hist,
                                                                  int nh) {
@@ -72,72 +131,82 @@ __global__ void __launch_bounds__(kStsThreads) sts_clear_kernel(unsigned int* do
   if (threadIdx.x == 0) *done = 0u;
 }
 
+__device__ __forceinline__ void add_dev(unsigned long long* p, unsigned long long v) {
+  if (v != 0ull) __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ void __launch_bounds__(kStsThreads) sts_pass_kernel(StsParams p) {
+  constexpr int T = kStsThreads;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x;
   const int G = p.G, nbins = p.nbins, k = p.k;
   const int nh = nbins * G;
-  unsigned long long* h = reinterpret_cast<unsigned long long*>(smem);             // [nbins][G]
-  double2* stage_ls = reinterpret_cast<double2*>(smem + sts_hist_lds_bytes(nh));  // {logit, S_{k-1}}
-  double* stage_y = reinterpret_cast<double*>(stage_ls + kStsThreads);            // label
+  // LDS: histogram [nbins][G], then the round's blocks {logit, S_{k-1}} and labels
+  unsigned long long* h = reinterpret_cast<unsigned long long*>(smem);
+  double2* stage_ls = reinterpret_cast<double2*>(smem + sts_hist_lds_bytes(nh));
+  double* stage_y = reinterpret_cast<double*>(stage_ls + T);
   __shared__ int last;
-  __shared__ long long best_e[kStsThreads];
-  __shared__ int best_g[kStsThreads];
+  __shared__ long long best_e[T];
+  __shared__ int best_g[T];
 
-  for (int i = tid; i < nh; i += kStsThreads) h[i] = 0ull;
+  for (int i = tid; i < nh; i += T) h[i] = 0ull;
 
   // temperature fitted at the previous position (applied while staging)
-  double inv_prev = 0.0;
-  if (k >= 2) inv_prev = 1.0 / double(p.grid[p.choice[k - 2]]);
+  double ninv_prev = 0.0;
+  if (k >= 2) ninv_prev = -1.0 / double(p.grid[p.choice[k - 2]]);
 
-  // candidate(s) of this thread: g = tid % G for G <= kStsThreads (tid / G
-  // picks which of the staged blocks it scores), else g = tid, tid + 1024, ...
-  const int nsub = G <= kStsThreads ? kStsThreads / G : 1;
-  const int sub = G <= kStsThreads ? tid / G : 0;
+  // A thread scores two candidates, g and g + slots, of one slot; slot =
+  // tid % slots when slots <= T (tid / slots picks which staged blocks),
+  // else slots tid, tid + T, ...
+  const int slots = (G + 1) / 2;
+  const bool resident = slots <= T;
+  const int nsub = resident ? T / slots : 1;
+  const int sub = resident ? tid / slots : 0;
   const bool active = sub < nsub;
+  const unsigned int row_bytes = unsigned(G) * 8u;   // < 2^24: a 24-bit multiply addresses a bin row
 
-  const int nchunks = (p.N + kStsThreads - 1) / kStsThreads;
+  const int nchunks = (p.N + T - 1) / T;
   for (int c = blockIdx.x; c < nchunks; c += gridDim.x) {
-    const int n0 = c * kStsThreads;
-    const int cnt = min(kStsThreads, p.N - n0);
-    __syncthreads();   // the previous chunk's readers are done with the stage
+    const int n0 = c * T;
+    const int cnt = min(T, p.N - n0);
+    __syncthreads();   // the previous round's readers are done with the stage
     if (tid < cnt) {
       const int n = n0 + tid;
       const size_t row = size_t(n) * size_t(p.gamma);
-      double s = 1.0;
+      double sv = 1.0;
       if (k >= 2) {
         const double s_prev = k >= 3 ? p.S[n] : 1.0;
-        s = s_prev * sigmoid_scaled(double(p.logit[row + k - 2]), inv_prev);
-        p.S[n] = s;
+        sv = s_prev * sigmoid_scaled(double(p.logit[row + k - 2]), ninv_prev);
+        p.S[n] = sv;
       }
-      stage_ls[tid] = make_double2(double(p.logit[row + k - 1]), s);
+      stage_ls[tid] = make_double2(double(p.logit[row + k - 1]), sv);
       stage_y[tid] = p.accepted[n] >= k ? 1.0 : 0.0;
     }
     __syncthreads();
     if (!active) continue;
-    for (int g = G <= kStsThreads ? tid % G : tid; g < G; g += kStsThreads) {
-      const double inv_t = 1.0 / double(p.grid[g]);
+    for (int sl = resident ? tid % slots : tid; sl < slots; sl += T) {
+      const int g1 = sl + slots;
+      const bool two = g1 < G;
+      const double ninv0 = -1.0 / double(p.grid[sl]);
+      const double ninv1 = two ? -1.0 / double(p.grid[g1]) : ninv0;
+      unsigned char* h0 = reinterpret_cast<unsigned char*>(h + sl);
+      unsigned char* h1 = reinterpret_cast<unsigned char*>(h + g1);
       for (int j = sub; j < cnt; j += nsub) {
         const double2 ls = stage_ls[j];
-        double pr, res;
-        {
-#pragma clang fp contract(off)
-          pr = ls.y * sigmoid_scaled(ls.x, inv_t);
-          res = (stage_y[j] - pr) * 4294967296.0;
+        const double y = stage_y[j];
+        const Scored s0 = score(ls.x, ls.y, y, ninv0, nbins);
+        atomicAdd(reinterpret_cast<unsigned long long*>(h0 + __umul24(s0.bin, row_bytes)), s0.q);
+        if (two) {
+          const Scored s1 = score(ls.x, ls.y, y, ninv1, nbins);
+          atomicAdd(reinterpret_cast<unsigned long long*>(h1 + __umul24(s1.bin, row_bytes)), s1.q);
         }
-        unsigned int b = static_cast<unsigned int>(pr * double(nbins));   // pr >= 0; NaN -> 0
-        b = min(b, unsigned(nbins - 1));
-        atomicAdd(&h[b * unsigned(G) + unsigned(g)], static_cast<unsigned long long>(rint_to_i64(res)));
       }
     }
   }
   __syncthreads();
 
   // add this workgroup's histogram to the device one, then arrive
-  for (int i = tid; i < nh; i += kStsThreads) {
-    const unsigned long long v = h[i];
-    if (v != 0ull) __hip_atomic_fetch_add(&p.hist[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  for (int i = tid; i < nh; i += T) add_dev(&p.hist[i], h[i]);
   wait_vmem();
   __syncthreads();
   if (tid == 0) {
@@ -152,7 +221,7 @@ __global__ void __launch_bounds__(kStsThreads) sts_pass_kernel(StsParams p) {
   long long my_e = -1;
   int my_g = 0;
   const double denom = 4294967296.0 * double(p.N);
-  for (int g = tid; g < G; g += kStsThreads) {
+  for (int g = tid; g < G; g += T) {
     long long e = 0;
     for (int m = 0; m < nbins; ++m) {
       const long long v = static_cast<long long>(load_dev(&p.hist[size_t(m) * G + g]));
@@ -167,11 +236,11 @@ __global__ void __launch_bounds__(kStsThreads) sts_pass_kernel(StsParams p) {
   best_e[tid] = my_e;
   best_g[tid] = my_g;
   __syncthreads();
-  for (int i = tid; i < nh; i += kStsThreads) store_dev(&p.hist[i], 0ull);
+  for (int i = tid; i < nh; i += T) store_dev(&p.hist[i], 0ull);
   if (tid == 0) {
     long long e = -1;
     int g = 0;
-    for (int t = 0; t < kStsThreads && t < G; ++t) {
+    for (int t = 0; t < T && t < G; ++t) {
       if (best_e[t] < 0) continue;
       if (e < 0 || best_e[t] < e || (best_e[t] == e && best_g[t] < g)) {
         e = best_e[t];
@@ -223,9 +292,13 @@ hipError_t launch_sts_fit(const StsArgs& a, hipStream_t stream) {
   p.done = reinterpret_cast<unsigned int*>(ws + L.ctrl);
   p.hist = reinterpret_cast<unsigned long long*>(ws + L.hist);
   p.S = reinterpret_cast<double*>(ws + L.S);
-  const int nchunks = (a.N + kStsThreads - 1) / kStsThreads;
-  const int nwg = std::max(1, std::min(nchunks, std::max(cus, 1)));
   const size_t lds = sts_lds_bytes(a.G, a.nbins);
+  int per_cu = 1;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&sts_pass_kernel),
+                                                   kStsThreads, lds);
+  if (e != hipSuccess) return e;
+  const int nchunks = (a.N + kStsThreads - 1) / kStsThreads;
+  const int nwg = std::max(1, std::min(nchunks, std::max(cus, 1) * std::max(per_cu, 1)));
   hipLaunchKernelGGL(sts_clear_kernel, dim3(1), dim3(kStsThreads), 0, stream, p.done, p.hist, a.G * a.nbins);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
