@@ -287,6 +287,62 @@ def schedule(surv, t_step, n_min: int):
     return lens, m_star, float(phi[m_star]) / TWO32
 
 
+def schedule_threshold(surv, tau: float):
+    """Static confidence threshold: the baseline the hardware-aware scheduler
+    replaces ([P-blog] §6 "Hardware-Aware Prefix Scheduler": existing work
+    verifies by a fixed confidence threshold; [P-news] "Confidence-scheduled
+    verification": offline threshold sweeps).
+
+    Reading: a request verifies the longest prefix of its drafts whose prefix
+    survival S_k is at least tau (compared in fp32); the threshold ignores
+    the batch and the step cost.  Returns (lens int32 [B], M = sum of lens)."""
+    S = np.asarray(surv, dtype=np.float32)
+    ok = S >= np.float32(tau)
+    lens = np.cumprod(ok, axis=1).sum(axis=1).astype(np.int32)
+    return lens, int(lens.sum())
+
+
+SERVE_POLICIES = ("global", "global_delayed2", "threshold")
+
+
+def serve(weights: dict, iters: list, anchor0, t_step, n_min: int, policy: str = "global", tau: float = 0.5,
+          sampling: str = "greedy"):
+    """Several drafting iterations of one batch chained as in serving: the
+    target's bonus token of iteration t is the anchor (first prediction
+    position) of iteration t + 1 ([P-blog] §3 "Speculative decoding" loop;
+    §4 parallel stage).  Each iteration drafts, schedules and verifies.
+
+    Policies for the verify lengths:
+      global          - the hardware-aware scheduler on this iteration's survivals;
+      global_delayed2 - the same scheduler on the survivals of iteration t - 2
+                        (scheduling from predictions two steps old, so the
+                        decision never waits for the current draft: [P-wisp]
+                        "Key Takeaways", asynchrony); iterations 0 and 1 use
+                        their own survivals (reading: no older predictions);
+      threshold       - schedule_threshold on this iteration's survivals.
+    `iters[t]` holds U, h, target and seed of iteration t.  Returns a dict of
+    per-iteration arrays (tokens, logit, conf, surv, lens, M, accepted,
+    bonus)."""
+    if policy not in SERVE_POLICIES:
+        raise ValueError(policy)
+    anchor = np.asarray(anchor0, dtype=np.int32)
+    out = {k: [] for k in ("tokens", "logit", "conf", "surv", "lens", "M", "accepted", "bonus")}
+    for t, it in enumerate(iters):
+        tok, zs, conf, surv = draft(anchor, it["U"], it["h"], weights["W1"], weights["W2"], weights["conf_w"],
+                                   weights["conf_b"], weights["sts_T"], sampling=sampling, seed=it["seed"])
+        if policy == "threshold":
+            lens, M = schedule_threshold(surv, tau)
+        else:
+            src = out["surv"][t - 2] if (policy == "global_delayed2" and t >= 2) else surv
+            lens, M, _ = schedule(src, t_step, n_min)
+        acc, bonus = verify(tok, it["target"], lens)
+        for k, v in (("tokens", tok), ("logit", zs), ("conf", conf), ("surv", surv), ("lens", lens), ("M", M),
+                     ("accepted", acc), ("bonus", bonus)):
+            out[k].append(v)
+        anchor = bonus
+    return {k: np.asarray(v) for k, v in out.items()}
+
+
 # ----------------------------------------------------------------------------
 # Verification
 # ----------------------------------------------------------------------------
