@@ -48,6 +48,12 @@ enum {
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;     /* storage of U, h, W1, W2 */
 typedef enum { DSPARK_GREEDY = 0, DSPARK_GUMBEL = 1 } dspark_sampling;
+/* Verify-length policy of dspark_serve. */
+typedef enum {
+  DSPARK_POLICY_GLOBAL = 0,           /* dspark_schedule on the iteration's own survivals */
+  DSPARK_POLICY_GLOBAL_DELAYED2 = 1,  /* dspark_schedule on the survivals of iteration t - 2 */
+  DSPARK_POLICY_THRESHOLD = 2         /* dspark_schedule_threshold on the iteration's survivals */
+} dspark_policy;
 
 /* Bytes of workspace dspark_markov_draft needs for this shape (a multiple of
  * 256).  Returns 0 for B*gamma == 0.  Needs no GPU. */
@@ -253,6 +259,69 @@ size_t dspark_sts_workspace_bytes(int N, int G, int n_bins);
 dspark_status dspark_sts_fit(
     int N, int gamma, const float* logit, const int32_t* accepted, const float* grid,
     int G, int n_bins, int32_t* choice, float* T_out, double* ece,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_schedule_threshold — the static confidence-threshold verify
+ * lengths that the hardware-aware scheduler replaces.
+ *
+ * Defined by: [P-blog] §6 "Hardware-Aware Prefix Scheduler" (existing work
+ * verifies by a static confidence threshold); [P-news] "Confidence-scheduled
+ * verification" (offline threshold sweeps).
+ *
+ *   lens[b] = largest l <= gamma with surv[b][j] >= tau for all j < l   (fp32)
+ *   m_out[0] = sum of lens
+ * The threshold ignores the batch size and the step cost.
+ *
+ * Arguments
+ *   surv fp32 [B][gamma]  prefix survivals;  tau  the threshold
+ *   lens int32 [B] out;  m_out int32 [1] out
+ * Limits: B * gamma < 2^31.
+ */
+dspark_status dspark_schedule_threshold(
+    int B, int gamma, const float* surv, float tau, int32_t* lens, int32_t* m_out, hipStream_t stream);
+
+/*
+ * dspark_serve — `iters` drafting iterations of one batch chained as in
+ * serving: draft (dspark_markov_draft), choose the verify lengths, verify
+ * (dspark_verify); the bonus tokens of iteration t are the anchors of
+ * iteration t + 1.  Everything is enqueued on `stream` without host
+ * synchronisation; each kernel is the one the single-call entry points run.
+ *
+ * Defined by: [P-blog] §3 "Speculative decoding" (draft, verify, keep the
+ * accepted prefix and the target's token, repeat) and §4 parallel stage
+ * (the anchor opens the next block); [P-blog] §6 and [P-wisp] "2. The
+ * Hardware-Aware Prefix Scheduler" (policy GLOBAL); [P-wisp] "Key
+ * Takeaways" (asynchrony: scheduling from the predictions of two steps
+ * earlier, policy GLOBAL_DELAYED2; iterations 0 and 1 use their own
+ * survivals); [P-blog] §6 (the static threshold, policy THRESHOLD).
+ *
+ * Arguments (t = 0..iters-1; per-iteration arrays are stacked, iteration-major)
+ *   iters                      iterations (0: no-op)
+ *   B, gamma, V, r, d, dtype   as dspark_markov_draft
+ *   anchor0 int32 [B]          anchors of iteration 0
+ *   U  [iters][B][gamma][V], h [iters][B][gamma][d]     base logits and hidden states
+ *   W1, W2, conf_w, conf_b, sts_T, mode                 as dspark_markov_draft
+ *   seed                       iteration t samples with seed + t (GUMBEL)
+ *   target int32 [iters][B][gamma + 1]                  the target's tokens
+ *   t_step, n_min, n_count     step-cost table as dspark_schedule (unused by THRESHOLD)
+ *   policy, tau                verify-length policy; tau used by THRESHOLD
+ *   tokens, logit, conf, surv  [iters][B][gamma] out   draft outputs
+ *   lens, accepted, bonus      int32 [iters][B] out
+ *   m_out                      int32 [iters] out       scheduled drafts per iteration
+ *   workspace                  as dspark_markov_draft (dspark_draft_workspace_bytes)
+ * Every argument is checked before the first launch; a HIP error later
+ * leaves the iterations before it enqueued.  Limits: those of
+ * dspark_markov_draft, and B * gamma <= 16384 for the GLOBAL policies.
+ */
+dspark_status dspark_serve(
+    int iters, int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+    const int32_t* anchor0, const void* U, const void* h, const void* W1, const void* W2,
+    const float* conf_w, float conf_b, const float* sts_T, dspark_sampling mode, uint64_t seed,
+    const int32_t* target, const double* t_step, int n_min, int n_count,
+    dspark_policy policy, float tau,
+    int32_t* tokens, float* logit, float* conf, float* surv,
+    int32_t* lens, int32_t* accepted, int32_t* bonus, int32_t* m_out,
     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code. */

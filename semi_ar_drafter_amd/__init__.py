@@ -6,5 +6,5 @@ The compute runs in hand-written HIP kernels for gfx950 behind the C ABI of
 marshals arguments: it passes device pointers and the current HIP stream.
 Importing the functions below fails loudly if the library is not built.
 """
-from .binding import (markov_draft, parallel_draft, schedule, sts_fit, verify, workspace_bytes,  # noqa: F401
-                      library_path)
+from .binding import (markov_draft, parallel_draft, schedule, schedule_threshold, serve, sts_fit,  # noqa: F401
+                      verify, workspace_bytes, library_path)

@@ -45,6 +45,11 @@ def _declare(lib):
     lib.dspark_schedule.restype = c_int
     lib.dspark_parallel_draft.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_int, c_u64, c_vp, c_vp, c_vp]
     lib.dspark_parallel_draft.restype = c_int
+    lib.dspark_schedule_threshold.argtypes = [c_int, c_int, c_vp, ctypes.c_float, c_vp, c_vp, c_vp]
+    lib.dspark_schedule_threshold.restype = c_int
+    lib.dspark_serve.argtypes = ([c_int] * 6 + [c_int] + [c_vp] * 6 + [ctypes.c_float, c_vp, c_int, c_u64] +
+                                 [c_vp, c_vp, c_int, c_int, c_int, ctypes.c_float] + [c_vp] * 9 + [c_size, c_vp])
+    lib.dspark_serve.restype = c_int
     lib.dspark_sts_workspace_bytes.argtypes = [c_int, c_int, c_int]
     lib.dspark_sts_workspace_bytes.restype = c_size
     lib.dspark_sts_fit.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
@@ -219,6 +224,70 @@ def sts_fit(logit, accepted, grid, n_bins: int, out=None, workspace=None):
                             _ptr(choice), _ptr(T), _ptr(ece), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
     _check(st)
     return choice, T, ece
+
+
+POLICIES = {"global": 0, "global_delayed2": 1, "threshold": 2}
+
+
+def schedule_threshold(surv, tau: float, out=None):
+    """Static-threshold verify lengths; returns (lens int32 [B], m int32 [1])."""
+    torch = _torch()
+    lib = load()
+    _need(surv, "surv", torch.float32)
+    B, gamma = surv.shape
+    dev = surv.device
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    lens, m = out
+    _check(lib.dspark_schedule_threshold(B, gamma, _ptr(surv), ctypes.c_float(tau), _ptr(lens), _ptr(m), _stream()))
+    return lens, m
+
+
+def serve(anchor0, U, h, W1, W2, conf_w, conf_b: float, sts_T, target, t_step, n_min: int,
+          policy: str = "global", tau: float = 0.5, mode: str = "greedy", seed: int = 0, out=None,
+          workspace=None):
+    """`iters` chained draft -> schedule -> verify iterations (U [iters, B,
+    gamma, V], h [iters, B, gamma, d], target int32 [iters, B, gamma + 1]).
+    Returns a dict of per-iteration device tensors: tokens, logit, conf, surv
+    [iters, B, gamma]; lens, accepted, bonus [iters, B]; m [iters]."""
+    torch = _torch()
+    lib = load()
+    _need(U, "U")
+    iters, B, gamma, V = U.shape
+    dev = U.device
+    dt = U.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("U must be float32 or bfloat16")
+    r = W1.shape[1]
+    d = h.shape[3]
+    _need(anchor0, "anchor0", torch.int32, (B,), dev)
+    _need(h, "h", dt, (iters, B, gamma, d), dev)
+    _need(W1, "W1", dt, (V, r), dev)
+    _need(W2, "W2", dt, (r, V), dev)
+    _need(conf_w, "conf_w", torch.float32, (d + r,), dev)
+    _need(sts_T, "sts_T", torch.float32, (gamma,), dev)
+    _need(target, "target", torch.int32, (iters, B, gamma + 1), dev)
+    _need(t_step, "t_step", torch.float64, None, dev)
+    if policy not in POLICIES:
+        raise ValueError(f"policy must be one of {sorted(POLICIES)}")
+    if out is None:
+        f = lambda *sh, dtype=torch.float32: torch.empty(sh, dtype=dtype, device=dev)  # noqa: E731
+        out = dict(tokens=f(iters, B, gamma, dtype=torch.int32), logit=f(iters, B, gamma), conf=f(iters, B, gamma),
+                   surv=f(iters, B, gamma), lens=f(iters, B, dtype=torch.int32),
+                   accepted=f(iters, B, dtype=torch.int32), bonus=f(iters, B, dtype=torch.int32),
+                   m=f(iters, dtype=torch.int32))
+    nbytes = workspace_bytes(B, gamma, V, r)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.dspark_serve(
+        iters, B, gamma, V, r, d, DSPARK_BF16 if dt == torch.bfloat16 else DSPARK_F32,
+        _ptr(anchor0), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2), _ptr(conf_w), ctypes.c_float(conf_b), _ptr(sts_T),
+        DSPARK_GUMBEL if mode == "gumbel" else DSPARK_GREEDY, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+        _ptr(target), _ptr(t_step), int(n_min), int(t_step.numel()), POLICIES[policy], ctypes.c_float(tau),
+        _ptr(out["tokens"]), _ptr(out["logit"]), _ptr(out["conf"]), _ptr(out["surv"]), _ptr(out["lens"]),
+        _ptr(out["accepted"]), _ptr(out["bonus"]), _ptr(out["m"]), _ptr(ws), ctypes.c_size_t(ws.numel()),
+        _stream())
+    _check(st)
+    return out
 
 
 def schedule(surv, t_step, n_min: int, out=None):

@@ -146,6 +146,67 @@ dspark_status dspark_parallel_draft(int B, int gamma, int V, dspark_dtype dtype,
   return DSPARK_OK;
 }
 
+dspark_status dspark_schedule_threshold(int B, int gamma, const float* surv, float tau, int32_t* lens,
+                                        int32_t* m_out, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || gamma < 0) return fail(DSPARK_ERR_INVALID_ARG, "negative size");
+  if (!m_out || (B > 0 && (!lens || (gamma > 0 && !surv)))) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  if ((long long)B * gamma > 0x7FFFFFFFLL) return fail(DSPARK_ERR_UNSUPPORTED, "B * gamma > 2^31 - 1");
+  hipError_t e = dspark::launch_schedule_threshold(B, gamma, surv, tau, lens, m_out, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return DSPARK_OK;
+}
+
+dspark_status dspark_serve(int iters, int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+                           const int32_t* anchor0, const void* U, const void* h, const void* W1, const void* W2,
+                           const float* conf_w, float conf_b, const float* sts_T, dspark_sampling mode,
+                           uint64_t seed, const int32_t* target, const double* t_step, int n_min, int n_count,
+                           dspark_policy policy, float tau, int32_t* tokens, float* logit, float* conf,
+                           float* surv, int32_t* lens, int32_t* accepted, int32_t* bonus, int32_t* m_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (iters < 0) return fail(DSPARK_ERR_INVALID_ARG, "negative iteration count");
+  if (policy != DSPARK_POLICY_GLOBAL && policy != DSPARK_POLICY_GLOBAL_DELAYED2 && policy != DSPARK_POLICY_THRESHOLD)
+    return fail(DSPARK_ERR_INVALID_ARG, "unknown scheduling policy");
+  if (B < 0 || gamma < 0 || V < 0 || r < 0 || d < 0) return fail(DSPARK_ERR_INVALID_ARG, "negative size");
+  if (iters == 0 || B == 0 || gamma == 0) return DSPARK_OK;
+  if (!target || !lens || !accepted || !bonus || !m_out || (policy != DSPARK_POLICY_THRESHOLD && !t_step))
+    return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  if (policy != DSPARK_POLICY_THRESHOLD) {
+    if (n_count < 1) return fail(DSPARK_ERR_INVALID_ARG, "empty step-cost table");
+    if (n_min > B || (long long)n_min + n_count - 1 < B)
+      return fail(DSPARK_ERR_INVALID_ARG, "step-cost table must cover n = B (n_min <= B <= n_min + n_count - 1)");
+    if ((long long)B * gamma > dspark::kMaxScheduleItems) return fail(DSPARK_ERR_UNSUPPORTED, "B * gamma > 16384");
+  }
+  const size_t elem = dtype == DSPARK_BF16 ? 2 : 4;
+  const size_t bg = size_t(B) * size_t(gamma);
+  for (int t = 0; t < iters; ++t) {
+    const int32_t* anchor = t == 0 ? anchor0 : bonus + size_t(t - 1) * B;
+    const unsigned char* Ut = static_cast<const unsigned char*>(U) + size_t(t) * bg * size_t(V) * elem;
+    const unsigned char* ht = h ? static_cast<const unsigned char*>(h) + size_t(t) * bg * size_t(d) * elem : nullptr;
+    float* surv_t = surv + size_t(t) * bg;
+    // iteration 0 validates the draft arguments before anything is enqueued;
+    // later iterations differ only by offsets that keep the same alignment
+    dspark_status st = dspark_markov_draft(B, gamma, V, r, d, dtype, anchor, Ut, ht, W1, W2, conf_w, conf_b, sts_T,
+                                           mode, seed + uint64_t(t), tokens + size_t(t) * bg, logit + size_t(t) * bg,
+                                           conf + size_t(t) * bg, surv_t, workspace, workspace_bytes, stream);
+    if (st != DSPARK_OK) return st;
+    hipError_t e;
+    if (policy == DSPARK_POLICY_THRESHOLD) {
+      e = dspark::launch_schedule_threshold(B, gamma, surv_t, tau, lens + size_t(t) * B, m_out + t, stream);
+    } else {
+      const float* src = (policy == DSPARK_POLICY_GLOBAL_DELAYED2 && t >= 2) ? surv + size_t(t - 2) * bg : surv_t;
+      e = dspark::launch_schedule(B, gamma, src, t_step, n_min, n_count, lens + size_t(t) * B, m_out + t, nullptr,
+                                  stream);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    e = dspark::launch_verify(B, gamma, tokens + size_t(t) * bg, target + size_t(t) * bg + size_t(t) * B,
+                              lens + size_t(t) * B, accepted + size_t(t) * B, bonus + size_t(t) * B, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return DSPARK_OK;
+}
+
 size_t dspark_sts_workspace_bytes(int N, int G, int n_bins) {
   if (N < 0 || G < 1 || n_bins < 1 || G > dspark::kMaxStsGrid || n_bins > dspark::kMaxStsBins) return 0;
   return dspark::sts_workspace_layout(N, G, n_bins).total;

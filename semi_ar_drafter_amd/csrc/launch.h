@@ -48,6 +48,9 @@ hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_
                            int n_count, int32_t* lens, int32_t* m_out, double* objective,
                            hipStream_t stream);
 
+hipError_t launch_schedule_threshold(int B, int gamma, const float* surv, float tau, int32_t* lens, int32_t* m_out,
+                                    hipStream_t stream);
+
 hipError_t launch_parallel_draft(int B, int gamma, int V, bool bf16, const void* U, bool gumbel, uint64_t seed,
                                  int32_t* tokens, float* logit, hipStream_t stream);
 

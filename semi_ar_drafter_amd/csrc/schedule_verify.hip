@@ -10,6 +10,10 @@
 // block scan of fixed-point gains, one fp64 division per candidate M, a
 // block arg-max, and a per-request count below the M*-th key.
 //
+// Static-threshold scheduler (the baseline of "DSpark: DeepSeek's new
+// speculative decoding work", §6): each request verifies the longest prefix
+// whose survival is at least a fixed threshold.
+//
 // Verify ("DeepSeek's DSpark just fixed the two things that held back faster
 // AI inference", opening; "DSpark: DeepSeek's new speculative decoding
 // work", §3): longest matching prefix of the scheduled drafts and the
@@ -145,6 +149,32 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
   }
 }
 
+// One workgroup: a thread per request (looping for B > 1024) scans its
+// survivals until the first one below tau; M is a block sum of the lengths.
+__global__ __launch_bounds__(kSchedThreads) void schedule_threshold_kernel(int B, int gamma,
+                                                                         const float* __restrict__ surv, float tau,
+                                                                         int32_t* lens, int32_t* m_out) {
+  __shared__ int part[kSchedWaves];
+  const int tid = threadIdx.x;
+  int acc = 0;
+  for (int b = tid; b < B; b += kSchedThreads) {
+    const float* row = surv + size_t(b) * gamma;
+    int l = 0;
+    while (l < gamma && row[l] >= tau) ++l;
+    lens[b] = l;
+    acc += l;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if ((tid & 63) == 0) part[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    int total = 0;
+    for (int w = 0; w < kSchedWaves; ++w) total += part[w];
+    m_out[0] = total;
+  }
+}
+
 __global__ __launch_bounds__(256) void verify_kernel(int B, int gamma, const int32_t* __restrict__ tokens,
                                                      const int32_t* __restrict__ target,
                                                      const int32_t* __restrict__ lens, int32_t* accepted,
@@ -166,6 +196,13 @@ hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_
                            int32_t* lens, int32_t* m_out, double* objective, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, B, gamma, surv, t_step, n_min,
                      n_count, lens, m_out, objective);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_threshold(int B, int gamma, const float* surv, float tau, int32_t* lens, int32_t* m_out,
+                                    hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_threshold_kernel, dim3(1), dim3(kSchedThreads), 0, stream, B, gamma, surv, tau, lens,
+                     m_out);
   return hipGetLastError();
 }
 

@@ -154,6 +154,42 @@ def test_sts_fit_validation(lib):
     assert "workspace" in lib.dspark_last_error().decode()
 
 
+def test_schedule_threshold_validation(lib):
+    st = lambda B=4, g=4, surv=P, tau=0.5, lens=P, m=P: lib.dspark_schedule_threshold(
+        B, g, surv, ctypes.c_float(tau), lens, m, NULL)
+    assert st(B=-1) == INVALID and st(g=-1) == INVALID
+    assert st(m=NULL) == INVALID and st(lens=NULL) == INVALID and st(surv=NULL) == INVALID
+    assert st(B=1 << 20, g=1 << 12) == UNSUPPORTED
+
+
+def test_serve_validation(lib):
+    ws_need = lib.dspark_draft_workspace_bytes(4, 4, 1024, 32)
+
+    def serve(iters=3, B=4, g=4, V=1024, r=32, d=16, dt=1, policy=0, n_min=4, n_count=17, ws=P, ws_bytes=None,
+              mode=0, **over):
+        ptr = dict(anchor=P, U=P, h=P, W1=P, W2=P, conf_w=P, sts_T=P, target=P, t_step=P, tokens=P, logit=P,
+                   conf=P, surv=P, lens=P, accepted=P, bonus=P, m=P)
+        ptr.update(over)
+        return lib.dspark_serve(iters, B, g, V, r, d, dt, ptr["anchor"], ptr["U"], ptr["h"], ptr["W1"], ptr["W2"],
+                                ptr["conf_w"], ctypes.c_float(1.0), ptr["sts_T"], mode, 0, ptr["target"],
+                                ptr["t_step"], n_min, n_count, policy, ctypes.c_float(0.5), ptr["tokens"],
+                                ptr["logit"], ptr["conf"], ptr["surv"], ptr["lens"], ptr["accepted"], ptr["bonus"],
+                                ptr["m"], ws, ctypes.c_size_t(ws_need if ws_bytes is None else ws_bytes), NULL)
+
+    assert serve(iters=-1) == INVALID and serve(policy=7) == INVALID and serve(B=-2) == INVALID
+    assert serve(iters=0) == OK and serve(B=0) == OK and serve(g=0) == OK      # no-ops: nothing launched
+    for k in ("target", "lens", "accepted", "bonus", "m", "t_step"):
+        assert serve(**{k: NULL}) == INVALID, k
+    assert serve(n_count=0) == INVALID
+    assert serve(n_min=5) == INVALID and serve(n_min=1, n_count=3) == INVALID   # table must cover n = B
+    assert serve(B=4096, g=8, n_count=40000, ws_bytes=1 << 40) == UNSUPPORTED  # global policy: B * gamma > 16384
+    # the draft arguments are checked by iteration 0 before anything is enqueued
+    assert serve(anchor=NULL) == INVALID and serve(W1=ctypes.c_void_p(0x10008)) == INVALID
+    assert serve(ws=NULL) == WORKSPACE and serve(ws_bytes=ws_need - 1) == WORKSPACE
+    assert serve(dt=5) == INVALID and serve(mode=4) == INVALID
+    assert lib.dspark_last_error().decode() != ""
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert lib.dspark_status_string(s).decode()
