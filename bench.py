@@ -17,7 +17,9 @@ a bounded sample of requests of the same workload; `ablation` times
 dspark_parallel_draft (drafting without the sequential head) on the same U,
 outside the timed step; `sts_fit` times dspark_sts_fit (fitting the 16
 confidence temperatures on 262144 synthetic calibration blocks, 128 candidate
-temperatures, 15 bins), also outside the step, against the VALU issue rate.
+temperatures, 15 bins), also outside the step, against the VALU issue rate;
+`serve` runs dspark_serve (4 chained iterations of the same batch, anchors
+taken from the previous bonus tokens) under each verify-length policy.
 """
 from __future__ import annotations
 
@@ -155,6 +157,45 @@ def time_sts_fit(torch, wl, sts_fit, reps: int = 10):
                          "kernel": f"sts_pass_kernel ({c.gamma} launches + 1 clear per fit)"}}
 
 
+def time_serve(torch, serve, w, anchor, U, h, W1, W2, conf_w, sts_T, target, t_step, mode, seed,
+               iters: int = 4, tau: float = 0.5):
+    """dspark_serve under each verify-length policy: `iters` chained
+    iterations of the benchmark batch (U, h and target repeated on the
+    device; the anchors chain through the bonus tokens)."""
+    Ur = U.unsqueeze(0).expand(iters, *U.shape).contiguous()
+    hr = h.unsqueeze(0).expand(iters, *h.shape).contiguous()
+    tr = target.unsqueeze(0).expand(iters, *target.shape).contiguous()
+    B = U.shape[0]
+    tab = w["t_step"]
+    res = {"workload": f"{iters} chained iterations of the benchmark batch (inputs repeated, anchors chained)",
+           "tau": tau}
+    for policy in ("global", "global_delayed2", "threshold"):
+        run = lambda: serve(anchor, Ur, hr, W1, W2, conf_w, w["conf_b"], sts_T, tr, t_step, w["n_min"],  # noqa: E731
+                            policy=policy, tau=tau, mode=mode, seed=seed)
+        run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            out = run()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / iters)
+        m = out["m"].cpu().numpy().astype(float)
+        acc = out["accepted"].cpu().numpy().astype(float)
+        committed = acc.sum() + iters * B
+        cost = float(sum(tab[B + int(x) - w["n_min"]] for x in m))
+        res[policy] = {"us_per_iteration": round(sorted(times)[1], 1),
+                       "verified_drafts_per_iteration": round(m.mean(), 1),
+                       "accepted_per_iteration": round(acc.sum() / iters, 1),
+                       "acceptance_rate": round(acc.sum() / max(m.sum(), 1.0), 4),
+                       "committed_per_iteration": round(committed / iters, 1),
+                       "committed_per_cost_unit": round(committed / cost, 3)}
+    del Ur, hr, tr
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +206,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sts", action="store_true", help="skip timing the temperature fit")
+    ap.add_argument("--no-serve", action="store_true", help="skip the serving-loop policy comparison")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (for HBM counter scaling) and exit")
     args = ap.parse_args()
@@ -177,7 +219,7 @@ def main():
     import numpy as np
     import torch
 
-    from semi_ar_drafter_amd import markov_draft, parallel_draft, schedule, sts_fit, verify
+    from semi_ar_drafter_amd import markov_draft, parallel_draft, schedule, serve, sts_fit, verify
     from semi_ar_drafter_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -292,6 +334,8 @@ def main():
     }
     if not args.no_sts:
         result["sts_fit"] = time_sts_fit(torch, wl, sts_fit)
+    if not args.no_serve:
+        result["serve"] = time_serve(torch, serve, w, anchor, U, h, W1, W2, conf_w, sts_T, target, t_step, mode, seed)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, min(args.cpu_rows, B), args.cpu_seconds)
         result["cpu_baseline"] = {"value": round(cb["tokens"] / cb["seconds"], 2), "unit": "drafted tokens/s",
