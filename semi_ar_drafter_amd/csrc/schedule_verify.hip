@@ -6,8 +6,8 @@
 // maximising (B + sum of scheduled survivals) / t_step(B + M).  Survival is
 // non-increasing along each request, so the best set of M drafts is the top
 // M by (S desc, request asc, position asc) and only M has to be searched.
-// One workgroup of 1024 threads: bitonic sort of 64-bit keys in LDS, a
-// block scan of fixed-point gains, one fp64 division per candidate M, a
+// One workgroup of 1024 threads: merge sort (bitonic above 8192 items) of
+// 64-bit keys in LDS, a block scan of fixed-point gains, one fp64 division per candidate M, a
 // block arg-max, and a per-request count below the M*-th key.
 //
 // Static-threshold scheduler (the baseline of "DSpark: DeepSeek's new
@@ -50,24 +50,81 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = B * gamma;
-  int n2 = 1;
+  int n2 = 4;
   while (n2 < n) n2 <<= 1;
 
-  for (int i = tid; i < n2; i += kSchedThreads)
-    keys[i] = (i < n) ? sched_key(surv[i], uint32_t(i)) : ~0ull;
-
-  // bitonic sort, ascending
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+  // Sort the keys ascending.  Up to half the key array, a merge sort: runs
+  // of 4 sorted in registers, then merge levels that ping-pong between the
+  // two halves of `keys`, each thread placing 4 outputs after a binary
+  // search for where its output range splits the two input runs (merge
+  // path).  Every level reads and writes the keys once; the bitonic network
+  // used for larger inputs passes over them once per stage.  Keys are
+  // distinct apart from the padding, so the order is the same either way.
+  const uint64_t* sorted = keys;
+  if (n2 <= kMaxScheduleItems / 2) {
+    uint64_t* src = keys;
+    uint64_t* dst = keys + kMaxScheduleItems / 2;
+    for (int q = tid * 4; q < n2; q += kSchedThreads * 4) {
+      uint64_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (q + j < n) ? sched_key(surv[q + j], uint32_t(q + j)) : ~0ull;
+      auto cs = [](uint64_t& a, uint64_t& b) {
+        const uint64_t lo = a < b ? a : b, hi = a < b ? b : a;
+        a = lo;
+        b = hi;
+      };
+      cs(v[0], v[1]);
+      cs(v[2], v[3]);
+      cs(v[0], v[2]);
+      cs(v[1], v[3]);
+      cs(v[1], v[2]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) src[q + j] = v[j];
+    }
+    for (int L = 4; L < n2; L <<= 1) {
       __syncthreads();
-      for (int t = tid; t < (n2 >> 1); t += kSchedThreads) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t a = keys[lo], b = keys[hi];
-        if ((a > b) == up) {
-          keys[lo] = b;
-          keys[hi] = a;
+      for (int o = tid * 4; o < n2; o += kSchedThreads * 4) {
+        const int base = o & ~(2 * L - 1);
+        const int d = o - base;
+        const uint64_t* A = src + base;
+        const uint64_t* Bv = src + base + L;
+        // i = outputs before o that come from A: the first i with A[i] > B[d-1-i]
+        int lo = d > L ? d - L : 0, hi = d < L ? d : L;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (A[mid] > Bv[d - 1 - mid])
+            hi = mid;
+          else
+            lo = mid + 1;
+        }
+        int i = lo, j = d - lo;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool take_a = j >= L || (i < L && A[i] <= Bv[j]);
+          dst[o + t] = take_a ? A[i++] : Bv[j++];
+        }
+      }
+      uint64_t* tmp = src;
+      src = dst;
+      dst = tmp;
+    }
+    sorted = src;
+  } else {
+    for (int i = tid; i < n2; i += kSchedThreads)
+      keys[i] = (i < n) ? sched_key(surv[i], uint32_t(i)) : ~0ull;
+    // bitonic sort, ascending
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        __syncthreads();
+        for (int t = tid; t < (n2 >> 1); t += kSchedThreads) {
+          const int lo = 2 * t - (t & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint64_t a = keys[lo], b = keys[hi];
+          if ((a > b) == up) {
+            keys[lo] = b;
+            keys[hi] = a;
+          }
         }
       }
     }
@@ -79,7 +136,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
   const int C = (m_max + kSchedThreads - 1) / kSchedThreads;
   const int p0 = min(tid * C, m_max), p1 = min(p0 + C, m_max);
   long long local = 0;
-  for (int p = p0; p < p1; ++p) local += gain_fixed(keys[p]);
+  for (int p = p0; p < p1; ++p) local += gain_fixed(sorted[p]);
   // block exclusive scan of the per-thread sums
   long long incl = local;
 #pragma unroll
@@ -101,7 +158,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
     best_m = 0;
   }
   for (int p = p0; p < p1; ++p) {
-    G += gain_fixed(keys[p]);
+    G += gain_fixed(sorted[p]);
     const int M = p + 1;
     const double phi = double(base + G) / t_step[B + M - n_min];
     if (phi > best) {
@@ -133,7 +190,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
         bm = red_m[w];
       }
     s_mstar = bm;
-    s_tau = (bm < n) ? keys[bm] : ~0ull;
+    s_tau = (bm < n) ? sorted[bm] : ~0ull;
     m_out[0] = bm;
     if (objective) objective[0] = bb / 4294967296.0;
   }

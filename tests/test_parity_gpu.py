@@ -200,6 +200,21 @@ def test_schedule_parity(B, g, mode):
         assert m == o_m and (lens == o_lens).all() and obj == o_obj, (table, m, o_m)
 
 
+@pytest.mark.parametrize("B,g", [(7, 5), (256, 16), (512, 16), (333, 21), (1024, 16)])
+def test_schedule_parity_rows_not_monotone(B, g):
+    """The sort inside the scheduler is a full sort: survivals in any order
+    (outside the documented contract) still give the oracle's top-M set."""
+    rng = np.random.default_rng(B * 7 + g)
+    S = rng.random((B, g)).astype(np.float32)
+    S[rng.random((B, g)) < 0.1] = np.float32(0.5)
+    n = np.arange(B, B + B * g + 1, dtype=np.float64)
+    t = 4.0 + 0.02 * n + 2e-5 * n * n
+    d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=B)
+    lens, m, obj = gpu_schedule(d, S)
+    o_lens, o_m, o_obj = orc.schedule(S, t, B)
+    assert m == o_m and (lens == o_lens).all() and obj == o_obj
+
+
 def test_schedule_table_offset_and_short_table():
     rng = np.random.default_rng(3)
     S = _rand_surv(rng, 40, 8, "random")
