@@ -131,7 +131,7 @@ def cpu_baseline(w, rows: int, min_seconds: float):
 
 def time_sts_fit(torch, wl, sts_fit, reps: int = 10):
     """Times dspark_sts_fit on the 262144-block calibration set (inputs in HBM)."""
-    c = wl.STS_CONFIGS[1]
+    c = wl.STS_WORKLOADS[1]
     cal = wl.make_sts_calibration(c)
     lo = torch.from_numpy(cal["logit"]).cuda()
     ac = torch.from_numpy(cal["accepted"]).cuda()
@@ -229,7 +229,7 @@ def main():
     if args.calibrate_copy:
         copy_calibration(args.calibrate_copy, 5)
         return
-    cfg = wl.CONFIGS[args.config]
+    cfg = wl.WORKLOADS[args.config]
     t_gen = time.perf_counter()
     w = wl.make_workload(cfg)
     print(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)

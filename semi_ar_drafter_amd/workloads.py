@@ -78,7 +78,7 @@ class Config:
         return dataclasses.replace(self, **kw)
 
 
-CONFIGS = {
+WORKLOADS = {
     0: Config(0, "tiny-fp32", 2, 4, 1024, 16, 64, "f32", (8.0, 8.0), (0.85, 0.85),
               ("linear", 1.0, 0.01)),
     1: Config(1, "qwen3-4b-latency", 1, 8, 151936, 256, 2560, "bf16", (8.0, 8.0),
@@ -223,7 +223,7 @@ class STSConfig:
         return dataclasses.replace(self, **kw)
 
 
-STS_CONFIGS = {
+STS_WORKLOADS = {
     0: STSConfig(200, "sts-small", 3000, 4, 24, 15),
     1: STSConfig(201, "sts-calibration-256k", 262144, 16, 128, 15),
 }

@@ -24,7 +24,7 @@ def _small(dtype="f32", **kw):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_lowrank_bias_equals_explicit_transition_matrix(dtype):
     """B = W1 W2 is a V x V matrix; the bias at step k is row x_{k-1} of it."""
-    w = wl.make_workload(wl.CONFIGS[0]) if dtype == "f32" else _small("bf16", V=512, r=32)
+    w = wl.make_workload(wl.WORKLOADS[0]) if dtype == "f32" else _small("bf16", V=512, r=32)
     trace = []
     tokens, zsel, conf, surv = orc.draft_workload(w, trace=trace)
     W1 = orc.widen(w["W1"])
@@ -44,7 +44,7 @@ def test_lowrank_bias_equals_explicit_transition_matrix(dtype):
 
 
 def test_argmax_is_numpy_first_occurrence_on_fp32_logits():
-    w = wl.make_workload(wl.CONFIGS[0])
+    w = wl.make_workload(wl.WORKLOADS[0])
     trace = []
     tokens, zsel, _, _ = orc.draft_workload(w, trace=trace)
     for st in trace:
@@ -129,7 +129,7 @@ def test_sts_temperature_scaling_properties():
 
 def test_survival_invariants():
     for cid in (0,):
-        w = wl.make_workload(wl.CONFIGS[cid])
+        w = wl.make_workload(wl.WORKLOADS[cid])
         _, _, conf, surv = orc.draft_workload(w)
         assert (surv[:, 0] == conf[:, 0]).all()
         assert (np.diff(surv, axis=1) <= 0).all()
@@ -158,7 +158,7 @@ def test_survival_is_expected_accepted_length_monte_carlo():
 def test_end_to_end_acceptance_statistics_tiny_config():
     """Not a parity pin: with the plant dominating, acceptance at position k
     is close to p (target agrees with the plant) times P(draft = plant)."""
-    cfg = wl.CONFIGS[0].replace(B=400)
+    cfg = wl.WORKLOADS[0].replace(B=400)
     w = wl.make_workload(cfg)
     tokens, _, _, _ = orc.draft_workload(w)
     hit = (tokens == w["plant"]).mean()

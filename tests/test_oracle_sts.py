@@ -68,7 +68,7 @@ def test_recovers_the_temperatures_of_the_acceptance_process():
 
 
 def test_each_position_is_the_grid_argmin_of_sklearn_ece():
-    w = wl.make_sts_calibration(wl.STS_CONFIGS[0])
+    w = wl.make_sts_calibration(wl.STS_WORKLOADS[0])
     L, a, grid, M = w["logit"].astype(np.float64), w["accepted"], w["grid"], w["n_bins"]
     choice, T, ece = orc.sts_fit(L.astype(np.float32), a, grid, M)
     prefix = np.ones(L.shape[0])
@@ -95,7 +95,7 @@ def test_all_accepted_or_all_rejected_closed_forms():
 
 
 def test_ties_resolved_to_the_first_entry_at_every_position():
-    w = wl.make_sts_calibration(wl.STS_CONFIGS[0])
+    w = wl.make_sts_calibration(wl.STS_WORKLOADS[0])
     grid = np.repeat(w["grid"], 2)                # every candidate twice
     c, T, e = orc.sts_fit(w["logit"], w["accepted"], grid, w["n_bins"])
     assert np.all(c % 2 == 0)
@@ -105,14 +105,14 @@ def test_ties_resolved_to_the_first_entry_at_every_position():
 
 
 def test_invariant_under_scaling_logits_and_grid_by_two():
-    w = wl.make_sts_calibration(wl.STS_CONFIGS[0])
+    w = wl.make_sts_calibration(wl.STS_WORKLOADS[0])
     c, T, e = orc.sts_fit(w["logit"], w["accepted"], w["grid"], w["n_bins"])
     c2, T2, e2 = orc.sts_fit(w["logit"] * np.float32(2), w["accepted"], w["grid"] * np.float32(2), w["n_bins"])
     assert np.array_equal(c, c2) and np.array_equal(T * 2, T2) and np.array_equal(e, e2)
 
 
 def test_invariant_under_permuting_blocks():
-    w = wl.make_sts_calibration(wl.STS_CONFIGS[0])
+    w = wl.make_sts_calibration(wl.STS_WORKLOADS[0])
     perm = np.random.default_rng(5).permutation(w["logit"].shape[0])
     c, T, e = orc.sts_fit(w["logit"], w["accepted"], w["grid"], w["n_bins"])
     cp, Tp, ep = orc.sts_fit(w["logit"][perm], w["accepted"][perm], w["grid"], w["n_bins"])
@@ -126,7 +126,7 @@ def test_no_blocks():
 
 
 def test_accepted_counts_saturate_at_both_ends():
-    w = wl.make_sts_calibration(wl.STS_CONFIGS[0])
+    w = wl.make_sts_calibration(wl.STS_WORKLOADS[0])
     a = w["accepted"].copy()
     gamma = w["logit"].shape[1]
     a2 = a.copy()

@@ -118,7 +118,7 @@ def test_matches_markov_draft_with_zero_transition():
 
 @pytest.mark.parametrize("cid,mode,nrows", [(3, "greedy", None), (4, "gumbel", 6)])
 def test_full_size(cid, mode, nrows):
-    cfg = wl.CONFIGS[cid]
+    cfg = wl.WORKLOADS[cid]
     say(f"[gen] config {cid} ...")
     w = wl.make_workload(cfg)
     d = to_device(w)

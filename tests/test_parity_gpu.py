@@ -85,7 +85,7 @@ def end_to_end(w, d, out):
 # small cases: whole batch against the oracle
 # --------------------------------------------------------------------------
 def test_tiny_fp32_config():
-    w = wl.make_workload(wl.CONFIGS[0])
+    w = wl.make_workload(wl.WORKLOADS[0])
     d, out = run_case(w)
     end_to_end(w, d, out)
 
@@ -242,7 +242,7 @@ def test_verify_parity_random():
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("cid,nrows", [(1, None), (2, 16), (3, 12), (4, 3)])
 def test_full_size_config(cid, nrows):
-    cfg = wl.CONFIGS[cid]
+    cfg = wl.WORKLOADS[cid]
     say(f"[gen] config {cid} ...")
     w = wl.make_workload(cfg)
     rows = None
@@ -256,7 +256,7 @@ def test_full_size_config(cid, nrows):
 def test_chained_gumbel_iterations():
     """Config 4 semantics at reduced batch: iteration t+1's anchor is
     iteration t's bonus token and its seed is seed0 + t."""
-    cfg = wl.CONFIGS[4].replace(B=24, cid=40)
+    cfg = wl.WORKLOADS[4].replace(B=24, cid=40)
     anchor = None
     for it in range(4):
         w = wl.make_workload(cfg, iteration=it, anchor=anchor)

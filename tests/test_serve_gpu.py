@@ -108,5 +108,5 @@ def test_serve_ragged_vocabulary_and_many_requests():
 def test_serve_qwen3_8b_shape():
     """B=64, gamma=16, V=151936, r=256, d=4096, three chained iterations;
     the draft is checked on a sample of requests, schedule and verify on all."""
-    g = serve_case(wl.CONFIGS[2], 3, "global", rows=[0, 17, 33, 63])
+    g = serve_case(wl.WORKLOADS[2], 3, "global", rows=[0, 17, 33, 63])
     assert g["m"].min() > 0

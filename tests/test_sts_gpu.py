@@ -80,7 +80,7 @@ def run_case(cfg):
 
 
 def test_small_calibration_set():
-    run_case(wl.STS_CONFIGS[0])
+    run_case(wl.STS_WORKLOADS[0])
 
 
 @pytest.mark.parametrize("N,gamma,G,n_bins", [
@@ -106,7 +106,7 @@ def test_no_blocks():
 
 
 def test_equal_candidates_choose_the_first():
-    w = wl.make_sts_calibration(wl.STS_CONFIGS[0])
+    w = wl.make_sts_calibration(wl.STS_WORKLOADS[0])
     grid = np.repeat(w["grid"], 2)
     c, T, e = gpu_fit(w["logit"], w["accepted"], grid, w["n_bins"])
     assert np.all(c % 2 == 0)
@@ -116,7 +116,7 @@ def test_equal_candidates_choose_the_first():
 
 def test_repeatable_for_any_workspace_contents():
     big = wl.make_sts_calibration(wl.STSConfig(450, "sts-repeat", 20000, 5, 48, 15))
-    small = wl.make_sts_calibration(wl.STS_CONFIGS[0])
+    small = wl.make_sts_calibration(wl.STS_WORKLOADS[0])
     r1 = gpu_fit(big["logit"], big["accepted"], big["grid"], big["n_bins"])
     r2 = gpu_fit(small["logit"], small["accepted"], small["grid"], small["n_bins"])
     r3 = gpu_fit(big["logit"], big["accepted"], big["grid"], big["n_bins"])
@@ -133,7 +133,7 @@ def test_repeatable_for_any_workspace_contents():
 
 
 def test_labels_saturate_at_both_ends():
-    w = wl.make_sts_calibration(wl.STS_CONFIGS[0])
+    w = wl.make_sts_calibration(wl.STS_WORKLOADS[0])
     a = w["accepted"].copy()
     a[a == w["cfg"].gamma] = 1000
     a[a == 0] = -5
@@ -146,7 +146,7 @@ def test_labels_saturate_at_both_ends():
 def test_full_calibration_set():
     """262144 blocks x 16 positions x 128 candidates x 15 bins: the whole
     oracle (about 20 s on one core) against the GPU."""
-    w, got = run_case(wl.STS_CONFIGS[1])
+    w, got = run_case(wl.STS_WORKLOADS[1])
     # the fit recovers the acceptance process's temperatures where labels are plentiful
     T, t_true = got[1], w["t_true"]
     assert np.all(np.abs(T[:10] / t_true[:10] - 1.0) < 0.08)
