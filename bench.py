@@ -1,7 +1,8 @@
 """Benchmark of the DSpark Markov-head draft -> prefix schedule -> verify path
 on one MI355X.
 
-One step = one pass of the whole path over one batch: dspark_markov_draft
+Before timing, steps run untimed for 0.2 s (clock ramp-up), then the W
+warm-up steps.  One step = one pass of the whole path over one batch: dspark_markov_draft
 (gamma dependent Markov-head steps with the confidence epilogue), then
 dspark_schedule on the drafted survivals, then dspark_verify against the
 target tokens.  Inputs are resident in HBM before timing starts.
@@ -11,7 +12,9 @@ greedy drafting, 64-point step-cost table 4 + 0.02 n + 2e-5 n^2 over
 n in [256, 4352] (synthetic inputs from the seeded generator).
 
 Prints one JSON line.  `value` = drafted tokens per second of the whole step
-(B * gamma / step time).  `roofline` rates the draft kernel against HBM
+(B * gamma / step time), with the drafting kernel in the exclusive launch mode
+(a plain launch: the benchmark is the only work on the device); the step
+time under the default cooperative launch is reported beside it.  `roofline` rates the draft kernel against HBM
 bandwidth with its algorithmic bytes; `cpu_baseline` times the CPU oracle on
 a bounded sample of requests of the same workload; `ablation` times
 dspark_parallel_draft (drafting without the sequential head) on the same U,
@@ -42,6 +45,7 @@ VALU_PEAK_GOPS = 256 * 64 * 2.4
 # y - p (1); rounding to 2^-32 (2); bin index (3); histogram address (1);
 # histogram add (1).
 STS_OPS_PER_EVAL = 34
+SETTLE_S = 0.2   # untimed steps before the warm-up: long enough for the clocks to settle
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # the draft kernel's device code (the traffic summary is tied to these files)
 DRAFT_SOURCES = [os.path.join(ROOT, "semi_ar_drafter_amd", "csrc", f) for f in ("markov_draft.hip", "device_util.h")]
@@ -158,7 +162,7 @@ def time_sts_fit(torch, wl, sts_fit, reps: int = 10):
 
 
 def time_serve(torch, serve, w, anchor, U, h, W1, W2, conf_w, sts_T, target, t_step, mode, seed,
-               iters: int = 4, tau: float = 0.5):
+               iters: int = 4, taus=(0.3, 0.5, 0.7)):
     """dspark_serve under each verify-length policy: `iters` chained
     iterations of the benchmark batch (U, h and target repeated on the
     device; the anchors chain through the bonus tokens)."""
@@ -167,9 +171,10 @@ def time_serve(torch, serve, w, anchor, U, h, W1, W2, conf_w, sts_T, target, t_s
     tr = target.unsqueeze(0).expand(iters, *target.shape).contiguous()
     B = U.shape[0]
     tab = w["t_step"]
-    res = {"workload": f"{iters} chained iterations of the benchmark batch (inputs repeated, anchors chained)",
-           "tau": tau}
-    for policy in ("global", "global_delayed2", "threshold"):
+    res = {"workload": f"{iters} chained iterations of the benchmark batch (inputs repeated, anchors chained)"}
+    runs = [("global", "global", 0.0), ("global_delayed2", "global_delayed2", 0.0)]
+    runs += [(f"threshold_{tau}", "threshold", tau) for tau in taus]
+    for label, policy, tau in runs:
         run = lambda: serve(anchor, Ur, hr, W1, W2, conf_w, w["conf_b"], sts_T, tr, t_step, w["n_min"],  # noqa: E731
                             policy=policy, tau=tau, mode=mode, seed=seed)
         run()
@@ -186,7 +191,7 @@ def time_serve(torch, serve, w, anchor, U, h, W1, W2, conf_w, sts_T, target, t_s
         acc = out["accepted"].cpu().numpy().astype(float)
         committed = acc.sum() + iters * B
         cost = float(sum(tab[B + int(x) - w["n_min"]] for x in m))
-        res[policy] = {"us_per_iteration": round(sorted(times)[1], 1),
+        res[label] = {"us_per_iteration": round(sorted(times)[1], 1),
                        "verified_drafts_per_iteration": round(m.mean(), 1),
                        "accepted_per_iteration": round(acc.sum() / iters, 1),
                        "acceptance_rate": round(acc.sum() / max(m.sum(), 1.0), 4),
@@ -207,6 +212,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sts", action="store_true", help="skip timing the temperature fit")
     ap.add_argument("--no-serve", action="store_true", help="skip the serving-loop policy comparison")
+    ap.add_argument("--draft-launch", choices=("exclusive", "cooperative"), default="exclusive",
+                    help="launch mode of the drafting kernel for the timed steps (the other is timed too)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (for HBM counter scaling) and exit")
     args = ap.parse_args()
@@ -219,7 +226,8 @@ def main():
     import numpy as np
     import torch
 
-    from semi_ar_drafter_amd import markov_draft, parallel_draft, schedule, serve, sts_fit, verify
+    from semi_ar_drafter_amd import (markov_draft, parallel_draft, schedule, serve, set_draft_launch, sts_fit,
+                                     verify)
     from semi_ar_drafter_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -261,6 +269,16 @@ def main():
         lens, m, obj = schedule(surv, t_step, w["n_min"], out=sched_out)
         verify(tok, target, lens, out=ver_out)
 
+    # The benchmark is the only work on the device, which is the exclusive
+    # launch mode's precondition; the default cooperative launch is timed too.
+    set_draft_launch(args.draft_launch)
+    # Untimed: run steps for SETTLE_S seconds first (the GPU's clocks ramp up
+    # over the first tens of milliseconds of work), then the W warm-up steps.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -279,6 +297,19 @@ def main():
     draft_ms = [a.elapsed_time(b) for a, b in ev]
     draft_avg = sum(draft_ms) / K
     value = B * g / (ms_step / 1e3)
+    other = "cooperative" if args.draft_launch == "exclusive" else "exclusive"
+    set_draft_launch(other)
+    for _ in range(2):
+        step()
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    o0.record()
+    for _ in range(K):
+        step()
+    o1.record()
+    torch.cuda.synchronize()
+    other_ms = o0.elapsed_time(o1) / K
+    set_draft_launch(args.draft_launch)
 
     # Ablation, outside the timed step: drafting with the parallel stage alone
     # (no sequential head) on the same U, to show what the Markov head costs.
@@ -318,6 +349,9 @@ def main():
         "config": {"workload": "markov-draft+schedule+verify", "B": B, "gamma": g, "V": cfg.V, "r": cfg.r,
                    "d": cfg.d, "storage": cfg.dtype, "sampling": cfg.sampling,
                    "sps_table": "64-point 4+0.02n+2e-5n^2, n in [256, 4352]"},
+        "draft_launch": {"mode": args.draft_launch, f"{other}_ms_per_step": round(other_ms, 5),
+                         "note": "exclusive = plain launch, the caller guaranteeing no other kernel on the device; "
+                                 "cooperative = the runtime's co-residency guarantee (default of the library)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",

@@ -48,6 +48,11 @@ enum {
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;     /* storage of U, h, W1, W2 */
 typedef enum { DSPARK_GREEDY = 0, DSPARK_GUMBEL = 1 } dspark_sampling;
+/* How dspark_markov_draft launches its persistent kernel (process-wide). */
+typedef enum {
+  DSPARK_LAUNCH_COOPERATIVE = 0,  /* cooperative launch: every workgroup is guaranteed resident (default) */
+  DSPARK_LAUNCH_EXCLUSIVE = 1     /* plain launch; the caller guarantees no other kernel runs meanwhile */
+} dspark_launch;
 /* Verify-length policy of dspark_serve. */
 typedef enum {
   DSPARK_POLICY_GLOBAL = 0,           /* dspark_schedule on the iteration's own survivals */
@@ -323,6 +328,28 @@ dspark_status dspark_serve(
     int32_t* tokens, float* logit, float* conf, float* surv,
     int32_t* lens, int32_t* accepted, int32_t* bonus, int32_t* m_out,
     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_set_draft_launch / dspark_get_draft_launch — how the drafting
+ * kernel is launched, for the whole process (dspark_markov_draft and
+ * dspark_serve).  Not an operation of the pages: a property of this
+ * implementation.
+ *
+ * The drafting kernel keeps one workgroup per compute unit resident for the
+ * whole call and synchronises them between draft positions, so every
+ * workgroup must run at the same time.  DSPARK_LAUNCH_COOPERATIVE (the
+ * default) asks the runtime for that guarantee; on ROCm it costs about
+ * 40 us per call.  DSPARK_LAUNCH_EXCLUSIVE launches plainly: the caller
+ * guarantees that no other kernel (from any stream or process) runs on the
+ * device while a drafting call runs, so the idle device places every
+ * workgroup at once — the usual situation of one serving loop per GPU.  If
+ * that guarantee is broken the kernel's bounded waits end the call after a
+ * few seconds with every token set to -1, and the workspace must be
+ * zero-filled again before its next use.
+ * Returns DSPARK_ERR_INVALID_ARG for an unknown mode.
+ */
+dspark_status dspark_set_draft_launch(dspark_launch mode);
+dspark_launch dspark_get_draft_launch(void);
 
 /* Static description of a status code. */
 const char* dspark_status_string(dspark_status s);

@@ -7,4 +7,4 @@ marshals arguments: it passes device pointers and the current HIP stream.
 Importing the functions below fails loudly if the library is not built.
 """
 from .binding import (markov_draft, parallel_draft, schedule, schedule_threshold, serve, sts_fit,  # noqa: F401
-                      verify, workspace_bytes, library_path)
+                      verify, workspace_bytes, library_path, set_draft_launch, get_draft_launch)

@@ -45,6 +45,10 @@ def _declare(lib):
     lib.dspark_schedule.restype = c_int
     lib.dspark_parallel_draft.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_int, c_u64, c_vp, c_vp, c_vp]
     lib.dspark_parallel_draft.restype = c_int
+    lib.dspark_set_draft_launch.argtypes = [c_int]
+    lib.dspark_set_draft_launch.restype = c_int
+    lib.dspark_get_draft_launch.argtypes = []
+    lib.dspark_get_draft_launch.restype = c_int
     lib.dspark_schedule_threshold.argtypes = [c_int, c_int, c_vp, ctypes.c_float, c_vp, c_vp, c_vp]
     lib.dspark_schedule_threshold.restype = c_int
     lib.dspark_serve.argtypes = ([c_int] * 6 + [c_int] + [c_vp] * 6 + [ctypes.c_float, c_vp, c_int, c_u64] +
@@ -227,6 +231,21 @@ def sts_fit(logit, accepted, grid, n_bins: int, out=None, workspace=None):
 
 
 POLICIES = {"global": 0, "global_delayed2": 1, "threshold": 2}
+LAUNCH_MODES = {"cooperative": 0, "exclusive": 1}
+
+
+def set_draft_launch(mode: str) -> None:
+    """Process-wide launch mode of the drafting kernel: "cooperative"
+    (default) or "exclusive" (the caller guarantees that no other kernel runs
+    on the device during a drafting call; saves the cooperative launch)."""
+    if mode not in LAUNCH_MODES:
+        raise ValueError(f"launch mode must be one of {sorted(LAUNCH_MODES)}")
+    _check(load().dspark_set_draft_launch(LAUNCH_MODES[mode]))
+
+
+def get_draft_launch() -> str:
+    v = load().dspark_get_draft_launch()
+    return {n: k for k, n in LAUNCH_MODES.items()}[v]
 
 
 def schedule_threshold(surv, tau: float, out=None):

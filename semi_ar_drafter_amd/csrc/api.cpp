@@ -2,6 +2,7 @@
 // validation, workspace sizing, status reporting and dispatch to the HIP
 // launchers.  Every check runs before anything is enqueued, so argument
 // errors are reported synchronously and without touching the GPU.
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 
@@ -25,6 +26,8 @@ dspark_status hip_fail(hipError_t e) {
   return DSPARK_ERR_HIP;
 }
 
+std::atomic<int> g_draft_launch{DSPARK_LAUNCH_COOPERATIVE};
+
 constexpr int kMaxGamma = 64;
 constexpr int kMaxD = 65536;
 constexpr int kMaxV = 1 << 24;
@@ -45,6 +48,16 @@ const char* dspark_status_string(dspark_status s) {
 }
 
 const char* dspark_last_error(void) { return g_last_error; }
+
+dspark_status dspark_set_draft_launch(dspark_launch mode) {
+  g_last_error[0] = '\0';
+  if (mode != DSPARK_LAUNCH_COOPERATIVE && mode != DSPARK_LAUNCH_EXCLUSIVE)
+    return fail(DSPARK_ERR_INVALID_ARG, "unknown launch mode");
+  g_draft_launch.store(int(mode));
+  return DSPARK_OK;
+}
+
+dspark_launch dspark_get_draft_launch(void) { return dspark_launch(g_draft_launch.load()); }
 
 size_t dspark_draft_workspace_bytes(int B, int gamma, int V, int r) {
   (void)V;
@@ -104,6 +117,7 @@ dspark_status dspark_markov_draft(int B, int gamma, int V, int r, int d, dspark_
   a.surv = surv;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
+  a.exclusive = g_draft_launch.load() == DSPARK_LAUNCH_EXCLUSIVE;
   const char* why = nullptr;
   hipError_t e = dspark::launch_markov_draft(a, stream, &why);
   if (why) return fail(DSPARK_ERR_UNSUPPORTED, "%s", why);

@@ -32,6 +32,7 @@ struct DraftArgs {
   float *logit, *conf, *surv;
   void* ws;
   size_t ws_bytes;
+  bool exclusive;   // plain launch: the caller guarantees nothing else runs on the device
 };
 
 // Workspace carve-up of the draft call (byte offsets, 256-aligned).

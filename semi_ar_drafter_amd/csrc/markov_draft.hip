@@ -1044,7 +1044,12 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   p.zpart = reinterpret_cast<float*>(ws + L.zpart);
   p.hdot = reinterpret_cast<double*>(ws + L.hdot);
 
+  // Every workgroup must be resident at once (grid barriers between draft
+  // positions; nwg <= one per compute unit).  The cooperative launch
+  // guarantees it; a plain launch gets it from an otherwise idle device,
+  // which the caller promises in exclusive mode.
   void* args[] = {&p};
+  if (a.exclusive) return hipLaunchKernel(kc.fn, dim3(nwg), dim3(kc.threads), args, 0, stream);
   return hipLaunchCooperativeKernel(kc.fn, dim3(nwg), dim3(kc.threads), args, 0, stream);
 }
 

@@ -190,6 +190,13 @@ def test_serve_validation(lib):
     assert lib.dspark_last_error().decode() != ""
 
 
+def test_draft_launch_mode_setting(lib):
+    assert lib.dspark_get_draft_launch() == 0                 # cooperative by default
+    assert lib.dspark_set_draft_launch(1) == OK and lib.dspark_get_draft_launch() == 1
+    assert lib.dspark_set_draft_launch(5) == INVALID and lib.dspark_get_draft_launch() == 1
+    assert lib.dspark_set_draft_launch(0) == OK and lib.dspark_get_draft_launch() == 0
+
+
 def test_status_strings(lib):
     for s in range(5):
         assert lib.dspark_status_string(s).decode()

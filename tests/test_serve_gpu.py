@@ -39,6 +39,13 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def test_threshold_empty_batch():
+    from semi_ar_drafter_amd import schedule_threshold
+    lens, m = schedule_threshold(torch.zeros((0, 4), dtype=torch.float32, device="cuda:0"), 0.5)
+    torch.cuda.synchronize()
+    assert lens.numel() == 0 and int(m.cpu().numpy()[0]) == 0
+
+
 @pytest.mark.parametrize("B,gamma", [(1, 1), (5, 4), (256, 16), (1000, 7), (3000, 16)])
 def test_threshold_bit_exact(B, gamma):
     from semi_ar_drafter_amd import schedule_threshold
