@@ -430,11 +430,16 @@ struct TileWork {
     }
   }
 
+  // The argmax runs at raised wave priority: it is the wave's serial
+  // stretch between two MFMA chains, and the other wave of the SIMD keeps
+  // the matrix unit busy meanwhile (measured: about 1.5 % faster calls).
   __device__ __forceinline__ void tile(f32x4_t (&acc)[NTF], int bt) const {
     mfma_chain(acc, bt);
+    __builtin_amdgcn_s_setprio(1);
     float bz;
     const uint64_t key = select(acc, bt, bz);
     merge(key, bz, bt);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // First three request tiles' loads, issued ahead of run() (possibly
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   if (tid == 0 && load_dev(&p.bar[0]) >= unsigned(nwg)) store_dev(&p.ctrl[1], 2u);
 
   // hdot for every (owned request, position): one (b, k) per wave at a time.
-  {
+  if constexpr (!FULL) {
     const st_t* h = static_cast<const st_t*>(p.h);
     const int nown = (B > wg) ? (B - 1 - wg) / nwg + 1 : 0;
     for (int q = wave; q < nown * gamma; q += NW) {
@@ -621,7 +626,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   // LDS (the embedding buffer is still free) a chunk of K rows at a time with
   // coalesced row loads; each wave then picks its fragments out of LDS.
   frag_t A[TPW][NKS];
-  {
+  if constexpr (!FULL) {
     constexpr int KCH0 = int(sizeof(lds_e) / (SLD * sizeof(st_t)));
     constexpr int KCH = (KCH0 >= R) ? R : (KCH0 / E::KS) * E::KS;   // K rows per chunk
     static_assert(KCH >= E::KS, "staging buffer too small");
@@ -687,6 +692,117 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       }
       __syncthreads();
     }
+  }
+  if constexpr (FULL) {
+    // Whole-tile path: W2 in chunks of one K step (32 rows) staged
+    // alternately through the embedding buffer and the U staging ring (both
+    // still free), with the global loads of the next two chunks in flight
+    // while a chunk is picked apart, one workgroup barrier per chunk.  The
+    // hidden-state dots run while the first two chunks load: the confidence
+    // weights are staged in the U ring first, and each wave keeps every
+    // 16-byte piece of a (b, k) row in flight at once.
+    constexpr int EPC = 8;                                    // bf16 per 16-byte piece
+    constexpr int PER = (E::KS * (CMAX / EPC) + NT - 1) / NT; // pieces per thread and chunk
+    static_assert(E::KS * SLD <= EBUF && E::KS * SLD * int(sizeof(st_t)) <= int(sizeof(lds_u)),
+                  "W2 staging buffers");
+    const st_t* W2 = static_cast<const st_t*>(p.W2);
+    const int col0 = wg_lo * 16;
+    const int cpr = wg_nt * 16 / EPC;                         // pieces per staged row
+    const int npc = E::KS * cpr;                              // pieces per chunk
+    // this thread's pieces of a chunk: element offsets in W2 (from the chunk's
+    // first row) and in the staging buffer (-1: none; such a slot loads the
+    // chunk's first piece again, unconditionally, so that the loads need no
+    // branches and stay in flight together, and stores nothing)
+    int goff[PER], loff[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * NT;
+      const int kr = i / cpr, c = i - kr * cpr;
+      goff[u] = (i < npc) ? kr * V + col0 + c * EPC : col0;
+      loff[u] = (i < npc) ? kr * SLD + c * EPC : -1;
+    }
+    auto issue = [&](u32x4_t (&q)[PER], int k0) {
+      const st_t* base = W2 + size_t(k0) * V;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) q[u] = *reinterpret_cast<const u32x4_t*>(base + goff[u]);
+    };
+    auto put = [&](const u32x4_t (&q)[PER], st_t* stg) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        if (loff[u] >= 0) *reinterpret_cast<u32x4_t*>(stg + loff[u]) = q[u];
+    };
+    u32x4_t qa[PER], qb[PER];
+    issue(qa, 0);
+    if (NKS > 1) issue(qb, E::KS);
+
+    const st_t* h = static_cast<const st_t*>(p.h);
+    const int nown = (B > wg) ? (B - 1 - wg) / nwg + 1 : 0;
+    constexpr int HJ = 16;                                     // 16-byte pieces per lane and row
+    const int hpc = p.d / 8;                                   // pieces per row
+    const bool fast_hd = (p.d % 8) == 0 && hpc <= 64 * HJ && p.d <= int(sizeof(lds_u) / sizeof(float)) &&
+                         (reinterpret_cast<uintptr_t>(h) & 15) == 0;
+    if (fast_hd) {
+      float* wl = reinterpret_cast<float*>(lds_u);
+      for (int i = tid; i < p.d; i += NT) wl[i] = p.conf_w[i];
+      __syncthreads();
+      for (int q = wave; q < nown * gamma; q += NW) {
+        const size_t hrow = size_t(wg + (q / gamma) * nwg) * gamma + q % gamma;
+        const u32x4_t* r = reinterpret_cast<const u32x4_t*>(h + hrow * p.d);
+        u32x4_t x[HJ];   // loaded unconditionally (clamped piece index), used where c < hpc
+#pragma unroll
+        for (int j = 0; j < HJ; ++j) x[j] = r[min(lane + 64 * j, hpc - 1)];
+        double acc = 0.0;
+#pragma unroll
+        for (int j = 0; j < HJ; ++j) {
+          const int c = lane + 64 * j;
+          if (c < hpc) {
+            const f32x4_t wa = *reinterpret_cast<const f32x4_t*>(wl + 8 * c);
+            const f32x4_t wb = *reinterpret_cast<const f32x4_t*>(wl + 8 * c + 4);
+            acc += double(wa[0]) * double(bf16_lo(x[j][0])) + double(wa[1]) * double(bf16_hi(x[j][0]));
+            acc += double(wa[2]) * double(bf16_lo(x[j][1])) + double(wa[3]) * double(bf16_hi(x[j][1]));
+            acc += double(wb[0]) * double(bf16_lo(x[j][2])) + double(wb[1]) * double(bf16_hi(x[j][2]));
+            acc += double(wb[2]) * double(bf16_lo(x[j][3])) + double(wb[3]) * double(bf16_hi(x[j][3]));
+          }
+        }
+        acc = wave_sum_f64(acc);
+        if (lane == 0) store_dev(&p.hdot[hrow], acc);
+      }
+    } else {
+      for (int q = wave; q < nown * gamma; q += NW) {
+        const int b = wg + (q / gamma) * nwg, kk = q % gamma;
+        const double v = hidden_dot(h + (size_t(b) * gamma + kk) * p.d, p.conf_w, p.d, lane);
+        if (lane == 0) store_dev(&p.hdot[size_t(b) * gamma + kk], v);
+      }
+    }
+    // (the hidden-state dots are visible to the other waves after the
+    // workgroup barriers below: wait_vmem orders the stores first)
+    wait_vmem();
+
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      st_t* stg = (ks & 1) ? reinterpret_cast<st_t*>(lds_u) : lds_e;
+      if (ks & 1) {
+        put(qb, stg);
+        if (ks + 2 < NKS) issue(qb, (ks + 2) * E::KS);
+      } else {
+        put(qa, stg);
+        if (ks + 2 < NKS) issue(qa, (ks + 2) * E::KS);
+      }
+      __syncthreads();   // chunk ks staged; the buffer's previous chunk was picked apart before the last barrier
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        if (nt > 0) {   // spare slots repeat columns the wave owns (pair layout)
+          const int c = (w_lo - wg_lo) * 16 + pair_col(t, li >> 2, nt, TPW) + (li & 3);
+          const int kr = E::KPL * lg;
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = uint32_t(stg[(kr + 2 * i) * SLD + c]) | (uint32_t(stg[(kr + 2 * i + 1) * SLD + c]) << 16);
+          A[t][ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
+        }
+      }
+    }
+    __syncthreads();   // both buffers are free again
   }
   for (int i = tid; i < kMaxOwnedRows; i += NT) lds_S[i] = 1.0f;
   for (int i = tid; i < R; i += NT) lds_we[i] = p.conf_w[p.d + i];
