@@ -114,10 +114,41 @@ def sigmoid64(x: np.ndarray) -> np.ndarray:
         return 1.0 / (1.0 + np.exp(-x))
 
 
+def bf16_round(x32: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bfloat16 (ties to even), returned as
+    uint16 bit patterns: add 0x7FFF plus the lowest kept bit to the fp32 bit
+    pattern and keep the top 16 bits (finite inputs)."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)).astype(np.uint16)
+
+
+def rnn_state_step(s_prev_bits: np.ndarray, decay: np.ndarray, e_bits: np.ndarray) -> np.ndarray:
+    """One step of the RNN head's recurrent state (reading of [P-blog] §4
+    "Two instantiations of the sequential block", RNN head: a recurrent state
+    that accumulates the whole prefix history within a block; the pages give
+    no equations).  Per rank channel j:
+
+        s_k[j] = bf16( fp32( fp32(a[j] * s_{k-1}[j]) + e_k[j] ) )
+
+    with e_k = W1[x_{k-1}] the embedding of the previous draft token, a the
+    per-channel decay (fp32, an input), s_0 = 0 and the state stored in bf16.
+    The product and the sum are separate fp32 operations (each rounded to
+    nearest).  a = 0 gives s_k = e_k, the Markov head; a = 1 sums the
+    embeddings of x_0 .. x_{k-1}.  bf16 inputs and output as uint16 bits."""
+    sp = widen(s_prev_bits).astype(np.float32)
+    e = widen(e_bits).astype(np.float32)
+    a = np.asarray(decay, dtype=np.float32)
+    t = (a * sp).astype(np.float32)
+    u = (t + e).astype(np.float32)
+    return bf16_round(u)
+
+
 def draft(anchor, U, h, W1, W2, conf_w, conf_b, sts_T, sampling: str = "greedy",
           seed: int = 0, rows=None, choose: Optional[Callable] = None,
-          trace: Optional[list] = None):
-    """Semi-autoregressive drafting with the Markov head.
+          trace: Optional[list] = None, decay=None):
+    """Semi-autoregressive drafting with the Markov head (decay None) or the
+    RNN head (decay = the per-channel decay a of rnn_state_step; bf16
+    storage only).
 
     For each request b (rows of the batch; every request's chain is
     independent) and each draft position k = 1..gamma:
@@ -151,6 +182,12 @@ def draft(anchor, U, h, W1, W2, conf_w, conf_b, sts_T, sampling: str = "greedy",
     whatever it returns.  `trace`, if a list, receives per-step dicts with the
     fp64 logits and the gathered embeddings.
 
+    RNN head ([P-blog] §4 sequential stage: the transition bias
+    B_k(x_0, x_{<k}, x_k) may depend on the whole prefix): steps 2-3 use the
+    recurrent state s_k of rnn_state_step in place of e, bias = s_k @ W2 (the
+    same logits projection); the confidence head keeps the Markov embedding e
+    of the previous draft token as its input ([P-blog] §5 names that input).
+
     Returns (tokens int32 [n, gamma], zsel fp32 [n, gamma], conf fp32,
     surv fp32), zsel being the unperturbed logit z_k(x_k).
     """
@@ -172,9 +209,18 @@ def draft(anchor, U, h, W1, W2, conf_w, conf_b, sts_T, sampling: str = "greedy",
     S = np.ones(n, dtype=np.float32)
     vv = np.arange(V, dtype=np.int64)
     ar = np.arange(n)
+    if decay is not None:
+        if np.asarray(W1).dtype != np.uint16:
+            raise TypeError("the RNN head is defined for bf16 storage")
+        state = np.zeros((n, r), dtype=np.uint16)               # s_0 = 0
     for k in range(1, gamma + 1):
         e = widen(W1[x_prev])                                   # step 1
-        z64 = widen(U[rows, k - 1]) + e @ W2f                   # steps 2-3
+        if decay is None:
+            q = e
+        else:
+            state = rnn_state_step(state, decay, W1[x_prev])
+            q = widen(state)
+        z64 = widen(U[rows, k - 1]) + q @ W2f                   # steps 2-3
         z = z64.astype(np.float32)
         if sampling == "greedy":
             s = z
@@ -194,7 +240,7 @@ def draft(anchor, U, h, W1, W2, conf_w, conf_b, sts_T, sampling: str = "greedy",
         conf[:, k - 1] = c
         surv[:, k - 1] = S
         if trace is not None:
-            trace.append(dict(k=k, z64=z64, z=z, s=s, e=e, ell=ell, x_prev=x_prev.copy()))
+            trace.append(dict(k=k, z64=z64, z=z, s=s, e=e, q=q, ell=ell, x_prev=x_prev.copy()))
         x_prev = x
     return tokens, zsel, conf, surv
 
@@ -462,9 +508,10 @@ def sts_fit(logit, accepted, grid, n_bins: int, choose: Optional[Callable] = Non
     return choice, T_out, ece
 
 
-def draft_workload(w: dict, rows=None, choose=None, trace=None, seed=None):
-    """Convenience wrapper over `draft` for a workload dictionary."""
+def draft_workload(w: dict, rows=None, choose=None, trace=None, seed=None, head: str = "markov"):
+    """Convenience wrapper over `draft` for a workload dictionary (head
+    "markov" or "rnn"; the RNN head takes the workload's decay)."""
     cfg = w["cfg"]
     return draft(w["anchor"], w["U"], w["h"], w["W1"], w["W2"], w["conf_w"], w["conf_b"],
                  w["sts_T"], sampling=cfg.sampling, seed=w["seed"] if seed is None else seed,
-                 rows=rows, choose=choose, trace=trace)
+                 rows=rows, choose=choose, trace=trace, decay=w["decay"] if head == "rnn" else None)

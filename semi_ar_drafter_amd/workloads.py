@@ -56,6 +56,7 @@ SEED_ROOT = 20260629
 _TAG_W1, _TAG_W2, _TAG_CONFW = 1, 2, 3
 _TAG_ANCHOR, _TAG_U, _TAG_PLANT, _TAG_H, _TAG_TGT_COIN, _TAG_TGT_UNI = 10, 11, 12, 13, 14, 15
 _TAG_STS_LOGIT, _TAG_STS_NOISE = 20, 21
+_TAG_DECAY = 30
 
 
 @dataclasses.dataclass(frozen=True)
@@ -151,7 +152,9 @@ def make_weights(cfg: Config) -> dict:
     conf_w = (_rng(cfg, _TAG_CONFW).standard_normal(d + r, dtype=np.float32)
               * np.float32(np.sqrt(0.05))).astype(np.float32)
     sts_T = (1.0 + 0.1 * np.arange(1, cfg.gamma + 1)).astype(np.float32)
-    return dict(W1=W1, W2=W2, conf_w=conf_w, conf_b=1.0, sts_T=sts_T)
+    # per-channel decay of the RNN head's recurrent state, uniform in [0.5, 0.95)
+    decay = (0.5 + 0.45 * _rng(cfg, _TAG_DECAY).random(r, dtype=np.float32)).astype(np.float32)
+    return dict(W1=W1, W2=W2, conf_w=conf_w, conf_b=1.0, sts_T=sts_T, decay=decay)
 
 
 def make_inputs(cfg: Config, iteration: int = 0, anchor: Optional[np.ndarray] = None) -> dict:
