@@ -64,6 +64,11 @@ typedef enum {
  * 256).  Returns 0 for B*gamma == 0.  Needs no GPU. */
 size_t dspark_draft_workspace_bytes(int B, int gamma, int V, int r);
 
+/* Bytes of workspace dspark_rnn_draft needs: the Markov-head workspace plus
+ * the recurrent state (2 x B x r bf16).  Returns 0 for B*gamma == 0 or
+ * r <= 0.  Needs no GPU. */
+size_t dspark_rnn_draft_workspace_bytes(int B, int gamma, int V, int r);
+
 /*
  * dspark_markov_draft — one block of semi-autoregressive drafting with the
  * Markov sequential head, its confidence head, Sequential Temperature
@@ -185,6 +190,42 @@ dspark_status dspark_schedule(
 dspark_status dspark_verify(
     int B, int gamma, const int32_t* tokens, const int32_t* target, const int32_t* lens,
     int32_t* accepted, int32_t* bonus, hipStream_t stream);
+
+/*
+ * dspark_rnn_draft — dspark_markov_draft with the RNN sequential head in
+ * place of the Markov head.
+ *
+ * Defined by: [P-blog] §4 "Semi-Autoregressive Generation" (sequential stage:
+ * the transition bias B_k(x_0, x_{<k}, x_k) may depend on the anchor and the
+ * whole draft prefix; "Two instantiations of the sequential block", RNN head:
+ * a recurrent state that accumulates the full prefix history within a
+ * block) and [P-blog] §5 (confidence head inputs: the hidden state and the
+ * Markov embedding of the previous draft token).  The pages give no
+ * equations for the RNN head; this library's reading is a per-channel
+ * decayed state, computed in fp32 and stored in bf16:
+ *   s_0     = 0
+ *   s_k[j]  = bf16( fp32( fp32(decay[j] * s_{k-1}[j]) + W1[x_{k-1}][j] ) )
+ *             (product and sum rounded separately, bf16 round to nearest even)
+ *   z_k(v)  = U[b][k-1][v] + sum_j s_k[j] * W2[j][v]      (fp32 accumulate)
+ * and x_k, c_k (with e = W1[x_{k-1}], not s_k) and S_k as in
+ * dspark_markov_draft.  decay = 0 gives exactly the Markov head; decay = 1
+ * sums the embeddings of x_0 .. x_{k-1}.
+ *
+ * Arguments as dspark_markov_draft, plus
+ *   decay   fp32  [r]     per-channel decay of the recurrent state
+ * with dtype DSPARK_BF16 only (DSPARK_ERR_UNSUPPORTED otherwise) and
+ *   workspace     >= dspark_rnn_draft_workspace_bytes(B, gamma, V, r) bytes,
+ *                 with the same zero-fill rule as dspark_markov_draft (the
+ *                 state section needs none).
+ * Errors and limits as dspark_markov_draft.
+ */
+dspark_status dspark_rnn_draft(
+    int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+    const int32_t* anchor, const void* U, const void* h, const void* W1, const void* W2,
+    const float* decay, const float* conf_w, float conf_b, const float* sts_T,
+    dspark_sampling mode, uint64_t seed,
+    int32_t* tokens, float* logit, float* conf, float* surv,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dspark_parallel_draft — drafting with the parallel stage alone: the

@@ -41,6 +41,13 @@ def _declare(lib):
                                         c_vp, c_f, c_vp, c_int, c_u64,
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]
     lib.dspark_markov_draft.restype = c_int
+    lib.dspark_rnn_draft_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+    lib.dspark_rnn_draft_workspace_bytes.restype = c_size
+    lib.dspark_rnn_draft.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int,
+                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                     c_vp, c_f, c_vp, c_int, c_u64,
+                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]
+    lib.dspark_rnn_draft.restype = c_int
     lib.dspark_schedule.argtypes = [c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
     lib.dspark_schedule.restype = c_int
     lib.dspark_parallel_draft.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_int, c_u64, c_vp, c_vp, c_vp]
@@ -174,6 +181,48 @@ def markov_draft(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, mode: str =
     st = lib.dspark_markov_draft(
         B, gamma, V, r, d, DSPARK_BF16 if dt == torch.bfloat16 else DSPARK_F32,
         _ptr(anchor), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2),
+        _ptr(conf_w), ctypes.c_float(conf_b), _ptr(sts_T),
+        DSPARK_GUMBEL if mode == "gumbel" else DSPARK_GREEDY, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+        _ptr(tokens), _ptr(logit), _ptr(conf), _ptr(surv),
+        _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    _check(st)
+    return tokens, logit, conf, surv
+
+
+def rnn_workspace_bytes(B: int, gamma: int, V: int, r: int) -> int:
+    return int(load().dspark_rnn_draft_workspace_bytes(B, gamma, V, r))
+
+
+def rnn_draft(anchor, U, h, W1, W2, decay, conf_w, conf_b: float, sts_T, mode: str = "greedy",
+              seed: int = 0, out=None, workspace=None):
+    """Draft gamma tokens per request with the RNN head (recurrent state
+    with per-channel decay `decay`, fp32 [r]); bfloat16 U, h, W1, W2; other
+    arguments and the result as markov_draft."""
+    torch = _torch()
+    lib = load()
+    _need(U, "U", torch.bfloat16)
+    B, gamma, V = U.shape
+    dev = U.device
+    r = W1.shape[1]
+    d = h.shape[2]
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(h, "h", torch.bfloat16, (B, gamma, d), dev)
+    _need(W1, "W1", torch.bfloat16, (V, r), dev)
+    _need(W2, "W2", torch.bfloat16, (r, V), dev)
+    _need(decay, "decay", torch.float32, (r,), dev)
+    _need(conf_w, "conf_w", torch.float32, (d + r,), dev)
+    _need(sts_T, "sts_T", torch.float32, (gamma,), dev)
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    tokens, logit, conf, surv = out
+    nbytes = rnn_workspace_bytes(B, gamma, V, r)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    st = lib.dspark_rnn_draft(
+        B, gamma, V, r, d, DSPARK_BF16,
+        _ptr(anchor), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2), _ptr(decay),
         _ptr(conf_w), ctypes.c_float(conf_b), _ptr(sts_T),
         DSPARK_GUMBEL if mode == "gumbel" else DSPARK_GREEDY, ctypes.c_uint64(seed & (2 ** 64 - 1)),
         _ptr(tokens), _ptr(logit), _ptr(conf), _ptr(surv),

@@ -63,35 +63,46 @@ size_t dspark_draft_workspace_bytes(int B, int gamma, int V, int r) {
   (void)V;
   (void)r;
   if (B <= 0 || gamma <= 0) return 0;
-  return dspark::draft_workspace_layout(B, gamma).total;
+  return dspark::draft_workspace_layout(B, gamma, 0).total;
 }
 
-dspark_status dspark_markov_draft(int B, int gamma, int V, int r, int d, dspark_dtype dtype,
-                                  const int32_t* anchor, const void* U, const void* h, const void* W1,
-                                  const void* W2, const float* conf_w, float conf_b, const float* sts_T,
-                                  dspark_sampling mode, uint64_t seed, int32_t* tokens, float* logit,
-                                  float* conf, float* surv, void* workspace, size_t workspace_bytes,
-                                  hipStream_t stream) {
+size_t dspark_rnn_draft_workspace_bytes(int B, int gamma, int V, int r) {
+  (void)V;
+  if (B <= 0 || gamma <= 0 || r <= 0) return 0;
+  return dspark::draft_workspace_layout(B, gamma, r).total;
+}
+
+namespace {
+
+// Shared by the Markov-head and RNN-head entry points (decay == nullptr: Markov).
+dspark_status draft_impl(int B, int gamma, int V, int r, int d, dspark_dtype dtype, const int32_t* anchor,
+                         const void* U, const void* h, const void* W1, const void* W2, const float* decay,
+                         bool rnn, const float* conf_w, float conf_b, const float* sts_T, dspark_sampling mode,
+                         uint64_t seed, int32_t* tokens, float* logit, float* conf, float* surv, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = '\0';
   if (B < 0 || gamma < 0 || V < 0 || r < 0 || d < 0)
     return fail(DSPARK_ERR_INVALID_ARG, "negative size");
   if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_INVALID_ARG, "unknown dtype");
   if (mode != DSPARK_GREEDY && mode != DSPARK_GUMBEL) return fail(DSPARK_ERR_INVALID_ARG, "unknown sampling mode");
+  if (rnn && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "the RNN head needs bf16 storage");
   if (B == 0 || gamma == 0) return DSPARK_OK;
   if (V < 1 || r < 1) return fail(DSPARK_ERR_INVALID_ARG, "V and r must be positive");
   if (!anchor || !U || !W1 || !W2 || !conf_w || !sts_T || !tokens || !logit || !conf || !surv ||
-      (d > 0 && !h))
+      (d > 0 && !h) || (rnn && !decay))
     return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
   if (gamma > kMaxGamma) return fail(DSPARK_ERR_UNSUPPORTED, "gamma > 64");
   if (d > kMaxD) return fail(DSPARK_ERR_UNSUPPORTED, "d > 65536");
   if (V > kMaxV) return fail(DSPARK_ERR_UNSUPPORTED, "V > 2^24");
   const int elem = dtype == DSPARK_BF16 ? 2 : 4;
   if (reinterpret_cast<uintptr_t>(W1) % 16 || reinterpret_cast<uintptr_t>(U) % elem ||
-      reinterpret_cast<uintptr_t>(W2) % elem || (h && reinterpret_cast<uintptr_t>(h) % elem))
+      reinterpret_cast<uintptr_t>(W2) % elem || (h && reinterpret_cast<uintptr_t>(h) % elem) ||
+      (rnn && reinterpret_cast<uintptr_t>(decay) % 4))
     return fail(DSPARK_ERR_INVALID_ARG, "misaligned tensor (W1 needs 16-byte alignment)");
-  const size_t need = dspark_draft_workspace_bytes(B, gamma, V, r);
+  const size_t need = rnn ? dspark_rnn_draft_workspace_bytes(B, gamma, V, r) : dspark_draft_workspace_bytes(B, gamma, V, r);
   if (!workspace || workspace_bytes < need)
-    return fail(DSPARK_ERR_WORKSPACE, "workspace missing or smaller than dspark_draft_workspace_bytes()");
+    return fail(DSPARK_ERR_WORKSPACE, rnn ? "workspace missing or smaller than dspark_rnn_draft_workspace_bytes()"
+                                          : "workspace missing or smaller than dspark_draft_workspace_bytes()");
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(DSPARK_ERR_WORKSPACE, "workspace not 256-byte aligned");
 
   dspark::DraftArgs a;
@@ -118,11 +129,33 @@ dspark_status dspark_markov_draft(int B, int gamma, int V, int r, int d, dspark_
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
   a.exclusive = g_draft_launch.load() == DSPARK_LAUNCH_EXCLUSIVE;
+  a.decay = rnn ? decay : nullptr;
   const char* why = nullptr;
   hipError_t e = dspark::launch_markov_draft(a, stream, &why);
   if (why) return fail(DSPARK_ERR_UNSUPPORTED, "%s", why);
   if (e != hipSuccess) return hip_fail(e);
   return DSPARK_OK;
+}
+
+}  // namespace
+
+dspark_status dspark_markov_draft(int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+                                  const int32_t* anchor, const void* U, const void* h, const void* W1,
+                                  const void* W2, const float* conf_w, float conf_b, const float* sts_T,
+                                  dspark_sampling mode, uint64_t seed, int32_t* tokens, float* logit,
+                                  float* conf, float* surv, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  return draft_impl(B, gamma, V, r, d, dtype, anchor, U, h, W1, W2, nullptr, false, conf_w, conf_b, sts_T, mode, seed,
+                    tokens, logit, conf, surv, workspace, workspace_bytes, stream);
+}
+
+dspark_status dspark_rnn_draft(int B, int gamma, int V, int r, int d, dspark_dtype dtype, const int32_t* anchor,
+                               const void* U, const void* h, const void* W1, const void* W2, const float* decay,
+                               const float* conf_w, float conf_b, const float* sts_T, dspark_sampling mode,
+                               uint64_t seed, int32_t* tokens, float* logit, float* conf, float* surv,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return draft_impl(B, gamma, V, r, d, dtype, anchor, U, h, W1, W2, decay, true, conf_w, conf_b, sts_T, mode, seed,
+                    tokens, logit, conf, surv, workspace, workspace_bytes, stream);
 }
 
 dspark_status dspark_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min, int n_count,

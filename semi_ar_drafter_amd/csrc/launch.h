@@ -33,13 +33,15 @@ struct DraftArgs {
   void* ws;
   size_t ws_bytes;
   bool exclusive;   // plain launch: the caller guarantees nothing else runs on the device
+  const float* decay = nullptr;   // non-null: RNN head with this per-channel state decay [r] (bf16 only)
 };
 
 // Workspace carve-up of the draft call (byte offsets, 256-aligned).
 struct DraftWorkspace {
-  size_t ctrl, bar, slots, zpart, hdot, total;
+  size_t ctrl, bar, slots, zpart, hdot, state, total;
 };
-DraftWorkspace draft_workspace_layout(int B, int gamma);
+// r_state: the RNN head's rank (its bf16 state [2][B][r] is carved out too), 0 for the Markov head.
+DraftWorkspace draft_workspace_layout(int B, int gamma, int r_state);
 
 // Returns hipSuccess or the first HIP error; sets *unsupported (with a reason)
 // when the shape is outside what the kernels handle.

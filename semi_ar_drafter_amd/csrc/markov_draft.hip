@@ -63,7 +63,27 @@ struct DraftParams {
   uint64_t* slots;     // [gamma][B] packed argmax keys
   float* zpart;        // [2][nwg][B] logit of each workgroup's local winner
   double* hdot;        // [B][gamma] hidden-state part of the confidence logit
+  const float* decay;  // RNN head: per-channel decay of the recurrent state [r]
+  uint16_t* state;     // RNN head: recurrent state, bf16 [2][B][r] (by step parity)
 };
+
+// RNN head state step for four channels (a reading of the RNN head, whose
+// equations the pages do not give): s = bf16(fp32(a * s_prev) + e), the
+// product and the sum rounded separately (no fused multiply-add), the bf16
+// rounding to nearest even by the hardware conversion.
+__device__ __forceinline__ u32x2_t rnn_step4(const float* a, u32x2_t sp, u32x2_t e) {
+#pragma clang fp contract(off)
+  const float spv[4] = {bf16_lo(sp.x), bf16_hi(sp.x), bf16_lo(sp.y), bf16_hi(sp.y)};
+  const float ev[4] = {bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = a[i] * spv[i];
+    const float u = t + ev[i];
+    o[i] = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(u)));
+  }
+  return u32x2_t{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+}
 
 template <bool BF16>
 struct Elem;
@@ -567,8 +587,9 @@ __device__ __forceinline__ double hidden_dot(const float* row, const float* w, i
 // FULL (bf16 only): V % 16 == 0, so every vocabulary tile is whole and rows
 // are 32-byte aligned, and every wave owns either no tile or at least two,
 // so the branch-free pair layout applies; otherwise the guarded path.
-template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL>
+template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL, bool RNN>
 __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p) {
+  static_assert(!RNN || BF16, "the RNN head is built for bf16 storage");
   typedef Elem<BF16> E;
   typedef typename E::store_t st_t;
   typedef typename E::frag_t frag_t;
@@ -589,6 +610,8 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   __shared__ double lds_hd[GR];
   __shared__ float lds_S[kMaxOwnedRows];
   __shared__ float lds_we[R];   // confidence weights of the Markov-embedding half
+  __shared__ float lds_dec[RNN ? R : 1];                // RNN head: decay
+  __shared__ double lds_ce[RNN ? kMaxOwnedRows : 1];    // RNN head: embedding half of owned rows' confidence dots
   // U staging ring of the whole-tile path: three slots of 3 KB per wave
   __shared__ __attribute__((aligned(16))) uint32_t lds_u[FULL ? NW * 3 * 768 : 4];
 
@@ -806,6 +829,8 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   }
   for (int i = tid; i < kMaxOwnedRows; i += NT) lds_S[i] = 1.0f;
   for (int i = tid; i < R; i += NT) lds_we[i] = p.conf_w[p.d + i];
+  if constexpr (RNN)
+    for (int i = tid; i < R; i += NT) lds_dec[i] = p.decay[i];
   for (int i = tid; i < GR; i += NT) lds_key[i] = 0ull;
 
   const st_t* U = static_cast<const st_t*>(p.U);
@@ -876,6 +901,23 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       }
       __syncthreads();
 
+      // RNN head: this thread's pieces (4 channels, 8 bytes) of the group's
+      // previous states s_{k-1}, loaded now so that they travel with the
+      // gather (device scope: written by the rows' owners before their
+      // arrival; s_0 = 0)
+      constexpr int PPR = R / 4;                                   // pieces per row
+      constexpr int SPT = RNN ? (GR * PPR + NT - 1) / NT : 1;     // pieces per thread
+      uint64_t sprev[SPT];
+      if constexpr (RNN) {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(p.state + size_t((k - 1) & 1) * B * R);
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+          const int q = min(tid + u * NT, rows * PPR - 1);
+          const int row = q / PPR;
+          sprev[u] = (k > 1) ? load_dev(src + (size_t(g0 + row) * R + (q - row * PPR) * 4) / 4) : 0ull;
+        }
+      }
+
       // 2. gather e = W1[x_{k-1}] for the group's rows (rounded up to whole request tiles) into LDS
       const int rows16 = (rows + 15) & ~15;
       if constexpr (BF16) {
@@ -921,6 +963,37 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
         pending = -1;
       }
 
+      // RNN head: the confidence head keeps the embedding e of the previous
+      // token as its input, so its embedding half is taken now; then the
+      // rows' states s_k = bf16(a s_{k-1} + e) replace e in LDS as the
+      // B operand, and each row's owner publishes its state for step k + 1.
+      if constexpr (RNN) {
+        const int j_lo = (g0 > wg) ? (g0 - wg + nwg - 1) / nwg : 0;
+        const int j_hi = (g0 + rows > wg) ? (g0 + rows - wg + nwg - 1) / nwg : 0;
+        for (int j = j_lo + wave; j < j_hi; j += NW) {
+          const int row = wg + j * nwg - g0;
+          double acc = 0.0;
+          for (int i = lane; i < R; i += 64) acc += double(lds_we[i]) * double(to_f32(lds_e[EL::at(row, i)]));
+          acc = wave_sum_f64(acc);
+          if (lane == 0) lds_ce[j - j_lo] = acc;
+        }
+        __syncthreads();
+        uint64_t* dst = reinterpret_cast<uint64_t*>(p.state + size_t(k & 1) * B * R);
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+          const int q = tid + u * NT;
+          if (q < rows * PPR) {
+            const int row = q / PPR, c = (q - row * PPR) * 4;
+            st_t* ep = lds_e + EL::at(row, c);
+            const u32x2_t sv = rnn_step4(&lds_dec[c], __builtin_bit_cast(u32x2_t, sprev[u]),
+                                         *reinterpret_cast<const u32x2_t*>(ep));
+            *reinterpret_cast<u32x2_t*>(ep) = sv;
+            if ((g0 + row) % nwg == wg) store_dev(dst + (size_t(g0 + row) * R + c) / 4, __builtin_bit_cast(uint64_t, sv));
+          }
+        }
+        __syncthreads();
+      }
+
       // 4. z = U_k + e W2 on MFMA, argmax in registers, per request tile
       if (nt > 0) work(k, g0, rows).run(pf0, pf1, pf2);
 
@@ -933,8 +1006,12 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           const int b = wg + j * nwg;
           const int row = b - g0;
           double acc = 0.0;
-          for (int i = lane; i < R; i += 64) acc += double(lds_we[i]) * double(to_f32(lds_e[EL::at(row, i)]));
-          acc = wave_sum_f64(acc);
+          if constexpr (RNN) {
+            acc = lds_ce[j - j_lo];
+          } else {
+            for (int i = lane; i < R; i += 64) acc += double(lds_we[i]) * double(to_f32(lds_e[EL::at(row, i)]));
+            acc = wave_sum_f64(acc);
+          }
           if (lane == 0) {
             const double ell = double(p.conf_b) + (lds_hd[row] + acc);
             const double c = 1.0 / (1.0 + exp(-ell / double(p.sts_T[k - 1])));
@@ -1017,34 +1094,35 @@ struct KernelChoice {
 
 constexpr int kDraftWaves = 8;
 
-template <bool BF16, int R, bool G>
+template <bool BF16, int R, bool G, bool RNN>
 KernelChoice pick_r(bool full) {
   constexpr int NW = kDraftWaves, GR = kMaxGroupRows;
   constexpr int TPW = BF16 ? 5 : 4;
   if constexpr (BF16) {
     if (full)
-      return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, true>),
+      return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, true, RNN>),
                           NW * 64, TPW};
   }
-  return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, false>), NW * 64,
-                      TPW};
+  return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, false, RNN>),
+                      NW * 64, TPW};
 }
 
 template <bool G>
-bool pick(bool bf16, int r, bool full, KernelChoice* out) {
+bool pick(bool bf16, int r, bool full, bool rnn, KernelChoice* out) {
   if (bf16) {
     switch (r) {
-      case 32: *out = pick_r<true, 32, G>(full); return true;
-      case 64: *out = pick_r<true, 64, G>(full); return true;
-      case 128: *out = pick_r<true, 128, G>(full); return true;
-      case 256: *out = pick_r<true, 256, G>(full); return true;
+      case 32: *out = rnn ? pick_r<true, 32, G, true>(full) : pick_r<true, 32, G, false>(full); return true;
+      case 64: *out = rnn ? pick_r<true, 64, G, true>(full) : pick_r<true, 64, G, false>(full); return true;
+      case 128: *out = rnn ? pick_r<true, 128, G, true>(full) : pick_r<true, 128, G, false>(full); return true;
+      case 256: *out = rnn ? pick_r<true, 256, G, true>(full) : pick_r<true, 256, G, false>(full); return true;
       default: return false;
     }
   }
+  if (rnn) return false;
   switch (r) {
-    case 16: *out = pick_r<false, 16, G>(full); return true;
-    case 32: *out = pick_r<false, 32, G>(full); return true;
-    case 64: *out = pick_r<false, 64, G>(full); return true;
+    case 16: *out = pick_r<false, 16, G, false>(full); return true;
+    case 32: *out = pick_r<false, 32, G, false>(full); return true;
+    case 64: *out = pick_r<false, 64, G, false>(full); return true;
     default: return false;
   }
 }
@@ -1074,7 +1152,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-DraftWorkspace draft_workspace_layout(int B, int gamma) {
+DraftWorkspace draft_workspace_layout(int B, int gamma, int r_state) {
   DraftWorkspace w;
   size_t off = 0;
   w.ctrl = off;
@@ -1087,6 +1165,8 @@ DraftWorkspace draft_workspace_layout(int B, int gamma) {
   off = align256(off + size_t(2) * kMaxDraftWorkgroups * B * sizeof(float));
   w.hdot = off;
   off = align256(off + size_t(B) * gamma * sizeof(double));
+  w.state = off;
+  off = align256(off + size_t(2) * B * size_t(r_state) * sizeof(uint16_t));
   w.total = off;
   return w;
 }
@@ -1094,9 +1174,11 @@ DraftWorkspace draft_workspace_layout(int B, int gamma) {
 hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported) {
   *unsupported = nullptr;
   KernelChoice kc;
-  if (!(a.gumbel ? pick<true>(a.bf16, a.r, false, &kc) : pick<false>(a.bf16, a.r, false, &kc))) {
-    *unsupported = a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
-                          : "fp32 drafting supports r in {16, 32, 64}";
+  const bool rnn = a.decay != nullptr;
+  if (!(a.gumbel ? pick<true>(a.bf16, a.r, false, rnn, &kc) : pick<false>(a.bf16, a.r, false, rnn, &kc))) {
+    *unsupported = rnn ? "the RNN head supports bf16 storage with r in {32, 64, 128, 256}"
+                       : a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
+                                : "fp32 drafting supports r in {16, 32, 64}";
     return hipSuccess;
   }
   DeviceInfo info;
@@ -1110,9 +1192,9 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   const bool full = (a.V % 16) == 0 && (tiles / nwg) / kDraftWaves >= 2;
   if (full) {
     if (a.gumbel)
-      pick<true>(a.bf16, a.r, true, &kc);
+      pick<true>(a.bf16, a.r, true, rnn, &kc);
     else
-      pick<false>(a.bf16, a.r, true, &kc);
+      pick<false>(a.bf16, a.r, true, rnn, &kc);
   }
   const int per_wg = (tiles + nwg - 1) / nwg;
   const int nwaves = kc.threads / 64;
@@ -1124,7 +1206,7 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
     *unsupported = "too many requests per workgroup for the confidence epilogue";
     return hipSuccess;
   }
-  const DraftWorkspace L = draft_workspace_layout(a.B, a.gamma);
+  const DraftWorkspace L = draft_workspace_layout(a.B, a.gamma, rnn ? a.r : 0);
   char* ws = static_cast<char*>(a.ws);
   DraftParams p;
   p.B = a.B;
@@ -1159,6 +1241,8 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   p.slots = reinterpret_cast<uint64_t*>(ws + L.slots);
   p.zpart = reinterpret_cast<float*>(ws + L.zpart);
   p.hdot = reinterpret_cast<double*>(ws + L.hdot);
+  p.decay = a.decay;
+  p.state = rnn ? reinterpret_cast<uint16_t*>(ws + L.state) : nullptr;
 
   // Every workgroup must be resident at once (grid barriers between draft
   // positions; nwg <= one per compute unit).  The cooperative launch

@@ -31,7 +31,7 @@ def to_device(w: dict, device="cuda:0") -> dict:
     return dict(anchor=dev(w["anchor"]), U=dev(w["U"]), h=dev(w["h"]), W1=dev(w["W1"]), W2=dev(w["W2"]),
                 conf_w=dev(w["conf_w"]), sts_T=dev(w["sts_T"]), target=dev(w["target"]),
                 t_step=dev(w["t_step"]), conf_b=float(w["conf_b"]), n_min=int(w["n_min"]),
-                seed=int(w["seed"]), mode=cfg.sampling)
+                seed=int(w["seed"]), mode=cfg.sampling, decay=dev(w["decay"]))
 
 
 def gpu_draft(d: dict):
@@ -39,6 +39,15 @@ def gpu_draft(d: dict):
     from semi_ar_drafter_amd import markov_draft
     out = markov_draft(d["anchor"], d["U"], d["h"], d["W1"], d["W2"], d["conf_w"], d["conf_b"], d["sts_T"],
                        mode=d["mode"], seed=d["seed"])
+    torch.cuda.synchronize()
+    return tuple(x.cpu().numpy() for x in out)
+
+
+def gpu_rnn_draft(d: dict):
+    import torch
+    from semi_ar_drafter_amd import rnn_draft
+    out = rnn_draft(d["anchor"], d["U"], d["h"], d["W1"], d["W2"], d["decay"], d["conf_w"], d["conf_b"], d["sts_T"],
+                    mode=d["mode"], seed=d["seed"])
     torch.cuda.synchronize()
     return tuple(x.cpu().numpy() for x in out)
 
@@ -57,9 +66,9 @@ class DraftParity:
                 and self.max_dsurv <= CONF_TOL)
 
 
-def check_draft(w: dict, gpu_out, rows=None) -> DraftParity:
-    """Runs the oracle on `rows` (default: all), replaying the GPU's token at
-    near ties, and compares element by element."""
+def check_draft(w: dict, gpu_out, rows=None, head: str = "markov") -> DraftParity:
+    """Runs the oracle (Markov or RNN head) on `rows` (default: all),
+    replaying the GPU's token at near ties, and compares element by element."""
     from oracle import dspark_oracle as orc
     g_tok, g_logit, g_conf, g_surv = gpu_out
     B = g_tok.shape[0]
@@ -88,7 +97,7 @@ def check_draft(w: dict, gpu_out, rows=None) -> DraftParity:
                 st.first_mismatch = st.first_mismatch or (int(rws[i]), k, int(x[i]), g)
         return x
 
-    o_tok, o_logit, o_conf, o_surv = orc.draft_workload(w, rows=rows, choose=choose)
+    o_tok, o_logit, o_conf, o_surv = orc.draft_workload(w, rows=rows, choose=choose, head=head)
     diff = o_tok != g_tok[rows]
     st.mismatches = max(st.mismatches, int(diff.sum()))
     st.max_dlogit = float(np.abs(o_logit - g_logit[rows]).max())

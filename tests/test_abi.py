@@ -78,6 +78,40 @@ def test_draft_validation(lib):
     assert draft(lib, gamma=0, anchor=NULL, U=NULL, ws=NULL, ws_bytes=0) == OK
 
 
+def rnn(lib, B=4, gamma=4, V=1024, r=32, d=16, dtype=1, mode=0, ws=P, ws_bytes=None, decay=P, **over):
+    ptrs = dict(anchor=P, U=P, h=P, W1=P, W2=P, conf_w=P, sts_T=P, tokens=P, logit=P, conf=P, surv=P)
+    ptrs.update(over)
+    if ws_bytes is None:
+        ws_bytes = lib.dspark_rnn_draft_workspace_bytes(max(B, 1), max(gamma, 1), V, r)
+    return lib.dspark_rnn_draft(B, gamma, V, r, d, dtype, ptrs["anchor"], ptrs["U"], ptrs["h"], ptrs["W1"],
+                                ptrs["W2"], decay, ptrs["conf_w"], ctypes.c_float(1.0), ptrs["sts_T"], mode,
+                                ctypes.c_uint64(0), ptrs["tokens"], ptrs["logit"], ptrs["conf"], ptrs["surv"],
+                                ws, ctypes.c_size_t(ws_bytes), NULL)
+
+
+def test_rnn_draft_validation(lib):
+    assert rnn(lib, dtype=0) == UNSUPPORTED                  # the RNN head is built for bf16 storage
+    assert rnn(lib, dtype=7) == INVALID
+    assert rnn(lib, decay=NULL) == INVALID
+    assert rnn(lib, decay=ctypes.c_void_p(0x10002)) == INVALID
+    for name in ("anchor", "U", "W1", "W2", "conf_w", "sts_T", "tokens", "logit", "conf", "surv"):
+        assert rnn(lib, **{name: NULL}) == INVALID, name
+    assert rnn(lib, r=48) == UNSUPPORTED
+    assert rnn(lib, gamma=65) == UNSUPPORTED
+    markov_bytes = lib.dspark_draft_workspace_bytes(4, 4, 1024, 32)
+    assert rnn(lib, ws_bytes=markov_bytes) == WORKSPACE      # the state section is missing
+    assert "dspark_rnn_draft_workspace_bytes" in lib.dspark_last_error().decode()
+    assert rnn(lib, B=0, anchor=NULL, U=NULL, ws=NULL, ws_bytes=0) == OK
+
+
+def test_rnn_workspace_size(lib):
+    assert lib.dspark_rnn_draft_workspace_bytes(0, 16, 151936, 256) == 0
+    assert lib.dspark_rnn_draft_workspace_bytes(256, 16, 151936, 0) == 0
+    m = lib.dspark_draft_workspace_bytes(256, 16, 151936, 256)
+    a = lib.dspark_rnn_draft_workspace_bytes(256, 16, 151936, 256)
+    assert a % 256 == 0 and a >= m + 2 * 256 * 256 * 2
+
+
 def test_workspace_size(lib):
     assert lib.dspark_draft_workspace_bytes(0, 16, 151936, 256) == 0
     a = lib.dspark_draft_workspace_bytes(256, 16, 151936, 256)
