@@ -22,7 +22,8 @@ outside the timed step; `sts_fit` times dspark_sts_fit (fitting the 16
 confidence temperatures on 262144 synthetic calibration blocks, 128 candidate
 temperatures, 15 bins), also outside the step, against the VALU issue rate;
 `serve` runs dspark_serve (4 chained iterations of the same batch, anchors
-taken from the previous bonus tokens) under each verify-length policy.
+taken from the previous bonus tokens) under each verify-length policy;
+`rnn_head` times dspark_rnn_draft (the RNN sequential head) on the same inputs.
 """
 from __future__ import annotations
 
@@ -226,8 +227,8 @@ def main():
     import numpy as np
     import torch
 
-    from semi_ar_drafter_amd import (markov_draft, parallel_draft, schedule, serve, set_draft_launch, sts_fit,
-                                     verify)
+    from semi_ar_drafter_amd import (markov_draft, parallel_draft, rnn_draft, schedule, serve, set_draft_launch,
+                                     sts_fit, verify)
     from semi_ar_drafter_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -326,6 +327,20 @@ def main():
     par_us = sum(a.elapsed_time(b) for a, b in pev) / len(pev) * 1e3
     u_bytes = B * g * cfg.V * (2 if cfg.dtype == "bf16" else 4)
 
+    # The RNN sequential head on the same inputs, outside the timed step.
+    decay = dev(w["decay"])
+    r_out = tuple(torch.empty((B, g), dtype=t, device="cuda")
+                  for t in (torch.int32, torch.float32, torch.float32, torch.float32))
+    for _ in range(2):
+        rnn_draft(anchor, U, h, W1, W2, decay, conf_w, w["conf_b"], sts_T, mode=mode, seed=seed, out=r_out)
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a, b in rev:
+        a.record()
+        rnn_draft(anchor, U, h, W1, W2, decay, conf_w, w["conf_b"], sts_T, mode=mode, seed=seed, out=r_out)
+        b.record()
+    torch.cuda.synchronize()
+    rnn_us = sum(a.elapsed_time(b) for a, b in rev) / len(rev) * 1e3
+
     abytes = algorithmic_bytes(cfg)
     achieved = abytes / (draft_avg / 1e3) / 1e9
     tflops = flops(cfg) / (draft_avg / 1e3) / 1e12
@@ -366,6 +381,14 @@ def main():
                      "note": "dspark_parallel_draft on the same U (no transition bias, no confidence), "
                              "timed separately from the step"},
     }
+    # RNN head: the Markov head's bytes plus the recurrent state (read and
+    # written once per step) and the decay vector
+    rbytes = abytes + 2 * B * g * cfg.r * 2 + cfg.r * 4
+    result["rnn_head"] = {"us_per_call": round(rnn_us, 2), "drafted_tokens_per_s": round(B * g / (rnn_us / 1e6), 1),
+                          "hbm_frac": round(rbytes / (rnn_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "marginal_us_vs_markov": round(rnn_us - draft_avg * 1e3, 2),
+                          "note": "dspark_rnn_draft (per-channel decayed recurrent state) on the same inputs, "
+                                  "timed separately from the step"}
     if not args.no_sts:
         result["sts_fit"] = time_sts_fit(torch, wl, sts_fit)
     if not args.no_serve:

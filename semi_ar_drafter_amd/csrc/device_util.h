@@ -104,6 +104,15 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 #endif
 }
 
+// The same load at device scope (cache policy sc1, as a relaxed agent-scope
+// atomic load uses): it reads what other workgroups published with
+// device-scope stores.
+__device__ __forceinline__ void load_lds16_dev(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 16);
+#endif
+}
+
 // LDS 64-bit atomic max and 32-bit store issued as plain ds_* instructions.
 // The compiler does not see them as LDS accesses, so it does not make them
 // wait for unrelated direct-to-LDS loads still in flight; in exchange the

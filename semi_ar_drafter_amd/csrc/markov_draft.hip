@@ -862,14 +862,22 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   // The next group's first three request tiles of U are loaded ahead of
   // time, before the slot reads and the gather that precede their use.
   typedef TileWork<BF16, R, TPW, GR, GUMBEL, TPW, !FULL> Work;
+  // (RNN head: the lane's addressing constants are recomputed per unit, the
+  // lane index being made opaque, instead of being kept live across the
+  // unit's state update, where they would spill to memory)
   auto work = [&](int k, int g0, int rows) {
+    int ln = lane;
+    if constexpr (RNN) asm volatile("" : "+v"(ln));
     return make_work<BF16, R, TPW, GR, GUMBEL, TPW, !FULL>(A, lds_e, U, g0, rows, B, gamma, k, V, w_lo, nt,
-                                                           p.vec_ok, li, lg, p.seed_lo, p.seed_hi, lds_key,
+                                                           p.vec_ok, ln & 15, ln >> 4, p.seed_lo, p.seed_hi, lds_key,
                                                            lds_z[wave], lds_u + (FULL ? wave * 3 * 768 : 0));
   };
   auto bar = [&](int g) { return p.bar + size_t(g) * kBarStride; };
   typename Work::Buf pf0, pf1, pf2;
-  if (nt > 0) work(1, 0, min(grs, B)).prefetch(pf0, pf1, pf2);
+  // (the whole-tile RNN kernel stages the previous states in the U ring at
+  // the start of a unit, so it loads a unit's first U tiles after that)
+  constexpr bool RING_STATE = RNN && FULL;
+  if (nt > 0 && !RING_STATE) work(1, 0, min(grs, B)).prefetch(pf0, pf1, pf2);
   int pending = -1;   // group whose arrival is still to be issued
 
   for (int k = 1; k <= gamma; ++k) {
@@ -900,23 +908,6 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
         if (own) lds_hd[tid] = load_dev(&p.hdot[size_t(b) * gamma + (k - 1)]);
       }
       __syncthreads();
-
-      // RNN head: this thread's pieces (4 channels, 8 bytes) of the group's
-      // previous states s_{k-1}, loaded now so that they travel with the
-      // gather (device scope: written by the rows' owners before their
-      // arrival; s_0 = 0)
-      constexpr int PPR = R / 4;                                   // pieces per row
-      constexpr int SPT = RNN ? (GR * PPR + NT - 1) / NT : 1;     // pieces per thread
-      uint64_t sprev[SPT];
-      if constexpr (RNN) {
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(p.state + size_t((k - 1) & 1) * B * R);
-#pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-          const int q = min(tid + u * NT, rows * PPR - 1);
-          const int row = q / PPR;
-          sprev[u] = (k > 1) ? load_dev(src + (size_t(g0 + row) * R + (q - row * PPR) * 4) / 4) : 0ull;
-        }
-      }
 
       // 2. gather e = W1[x_{k-1}] for the group's rows (rounded up to whole request tiles) into LDS
       const int rows16 = (rows + 15) & ~15;
@@ -954,6 +945,18 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           }
         }
       }
+      // whole-tile RNN kernel: the group's previous states s_{k-1} (rows
+      // contiguous in the state buffer) into the U ring, 16 bytes per lane,
+      // with the gather (device scope: written by the rows' owners before
+      // their arrival)
+      if constexpr (RING_STATE) {
+        if (k > 1) {
+          const char* src = reinterpret_cast<const char*>(p.state + (size_t((k - 1) & 1) * B + g0) * R);
+          const int nbytes = rows * R * 2;
+          for (int i = wave; i * 1024 < nbytes; i += NW)
+            if (i * 1024 + lane * 16 < nbytes) load_lds16_dev(src + i * 1024 + lane * 16, lds_u + i * 256);
+        }
+      }
       // outputs of step k-1 for owned rows, overlapping the gather
       if (own && k > 1) emit(g0 + tid, k - 1, own_key);
       wait_vmem();   // this wave's direct-to-LDS loads have landed (and its earlier atomics are done)
@@ -977,21 +980,45 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           acc = wave_sum_f64(acc);
           if (lane == 0) lds_ce[j - j_lo] = acc;
         }
-        __syncthreads();
+        __syncthreads();   // every wave has read e before the states replace it
+        // this thread's pieces (4 channels, 8 bytes) of the previous states
+        // s_{k-1}: from the U ring (whole-tile kernel) or from the state
+        // buffer, four in flight at a time (guarded kernel; device scope:
+        // written by the rows' owners before their arrival); s_0 = 0
+        constexpr int PPR = R / 4;                                // pieces per row
+        constexpr int SPT = (GR * PPR + NT - 1) / NT;             // pieces per thread
+        constexpr int BATCH = SPT < 4 ? SPT : 4;
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(p.state + size_t((k - 1) & 1) * B * R);
         uint64_t* dst = reinterpret_cast<uint64_t*>(p.state + size_t(k & 1) * B * R);
+#pragma unroll 1
+        for (int u0 = 0; u0 < SPT; u0 += BATCH) {
+          uint64_t sprev[BATCH];
 #pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-          const int q = tid + u * NT;
-          if (q < rows * PPR) {
-            const int row = q / PPR, c = (q - row * PPR) * 4;
-            st_t* ep = lds_e + EL::at(row, c);
-            const u32x2_t sv = rnn_step4(&lds_dec[c], __builtin_bit_cast(u32x2_t, sprev[u]),
-                                         *reinterpret_cast<const u32x2_t*>(ep));
-            *reinterpret_cast<u32x2_t*>(ep) = sv;
-            if ((g0 + row) % nwg == wg) store_dev(dst + (size_t(g0 + row) * R + c) / 4, __builtin_bit_cast(uint64_t, sv));
+          for (int u = 0; u < BATCH; ++u) {
+            const int q = min(tid + (u0 + u) * NT, rows * PPR - 1);   // clamped: always a valid address
+            const int row = q / PPR;
+            if constexpr (RING_STATE)
+              sprev[u] = (k > 1) ? reinterpret_cast<const uint64_t*>(lds_u)[q] : 0ull;
+            else
+              sprev[u] = (k > 1) ? load_dev(src + (size_t(g0 + row) * R + (q - row * PPR) * 4) / 4) : 0ull;
+          }
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int q = tid + (u0 + u) * NT;
+            if (q < rows * PPR) {
+              const int row = q / PPR, c = (q - row * PPR) * 4;
+              st_t* ep = lds_e + EL::at(row, c);
+              const u32x2_t sv = rnn_step4(&lds_dec[c], __builtin_bit_cast(u32x2_t, sprev[u]),
+                                           *reinterpret_cast<const u32x2_t*>(ep));
+              *reinterpret_cast<u32x2_t*>(ep) = sv;
+              if ((g0 + row) % nwg == wg)
+                store_dev(dst + (size_t(g0 + row) * R + c) / 4, __builtin_bit_cast(uint64_t, sv));
+            }
           }
         }
         __syncthreads();
+        if constexpr (RING_STATE)   // the ring is free again: this unit's first U tiles
+          if (nt > 0) work(k, g0, rows).prefetch(pf0, pf1, pf2);
       }
 
       // 4. z = U_k + e W2 on MFMA, argmax in registers, per request tile
@@ -1049,7 +1076,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       if (!last && nt > 0) {
         const int nk = (grp + 1 < ngroups) ? k : k + 1;
         const int ng0 = (grp + 1 < ngroups) ? g0 + grs : 0;
-        work(nk, ng0, min(grs, B - ng0)).prefetch(pf0, pf1, pf2);
+        if constexpr (!RING_STATE) work(nk, ng0, min(grs, B - ng0)).prefetch(pf0, pf1, pf2);
       }
     }
   }
