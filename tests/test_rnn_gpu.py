@@ -44,6 +44,10 @@ CASES = [
     (140, 4, 69632, 256, 64, "greedy"),       # whole-tile kernel, two groups
     (130, 3, 69632, 256, 64, "gumbel"),
     (64, 4, 70001, 256, 64, "greedy"),        # guarded kernel at a large, odd vocabulary
+    (1, 8, 151936, 256, 64, "greedy"),        # one request at the full vocabulary (latency shape)
+    (3, 64, 2048, 32, 16, "greedy"),          # the longest block (gamma = 64): 63 state steps
+    (256, 2, 151936, 256, 32, "gumbel"),      # whole-tile kernel, two full groups, Gumbel-max
+    (17, 3, 69648, 64, 16, "greedy"),         # whole-tile kernel, rank 64, ragged single group
 ]
 
 
