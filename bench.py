@@ -349,7 +349,7 @@ def main():
           f"wall {wall:.3f}s", file=sys.stderr, flush=True)
 
     result = {
-        "metric": "drafted tokens/s at V=151936 r=256 gamma=16 B=256; % of HBM roofline",
+        "metric": f"drafted tokens/s at V={cfg.V} r={cfg.r} \u03b3={g} B={B}; % of HBM roofline",
         "value": round(value, 1),
         "unit": "drafted tokens/s",
         "n_gpus": 1,
