@@ -240,7 +240,8 @@ def main():
         return
     cfg = wl.WORKLOADS[args.config]
     t_gen = time.perf_counter()
-    w = wl.make_workload(cfg)
+    w = wl.make_workload(cfg, progress=lambda b: print(f"[bench] generating {cfg.name}: request {b}/{cfg.B}",
+                                                         file=sys.stderr, flush=True))
     print(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
     def dev(a):

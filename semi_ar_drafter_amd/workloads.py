@@ -157,8 +157,9 @@ def make_weights(cfg: Config) -> dict:
     return dict(W1=W1, W2=W2, conf_w=conf_w, conf_b=1.0, sts_T=sts_T, decay=decay)
 
 
-def make_inputs(cfg: Config, iteration: int = 0, anchor: Optional[np.ndarray] = None) -> dict:
-    """Per-iteration inputs: anchor, U (with plants), h, plant ids, targets."""
+def make_inputs(cfg: Config, iteration: int = 0, anchor: Optional[np.ndarray] = None, progress=None) -> dict:
+    """Per-iteration inputs: anchor, U (with plants), h, plant ids, targets.
+    `progress(b)`, if given, is called every 64 requests of the U loop."""
     B, g, V, d = cfg.B, cfg.gamma, cfg.V, cfg.d
     if anchor is None:
         anchor = _rng(cfg, _TAG_ANCHOR, iteration).integers(0, V, size=B, dtype=np.int64)
@@ -171,6 +172,8 @@ def make_inputs(cfg: Config, iteration: int = 0, anchor: Optional[np.ndarray] = 
     su = np.float32(np.sqrt(2.0))
     rows = np.arange(g)
     for b in range(B):          # one request at a time bounds host memory
+        if progress is not None and b % 64 == 0:
+            progress(b)
         x = ru.standard_normal((g, V), dtype=np.float32) * su
         x[rows, plant[b]] += s_k
         U[b] = _store(x, cfg.dtype)
@@ -190,9 +193,9 @@ def make_inputs(cfg: Config, iteration: int = 0, anchor: Optional[np.ndarray] = 
                 t_step=t_step, n_min=n_min, seed=int(seed), iteration=iteration)
 
 
-def make_workload(cfg: Config, iteration: int = 0, anchor: Optional[np.ndarray] = None) -> dict:
+def make_workload(cfg: Config, iteration: int = 0, anchor: Optional[np.ndarray] = None, progress=None) -> dict:
     w = make_weights(cfg)
-    w.update(make_inputs(cfg, iteration, anchor))
+    w.update(make_inputs(cfg, iteration, anchor, progress))
     w["cfg"] = cfg
     return w
 
