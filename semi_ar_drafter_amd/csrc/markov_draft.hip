@@ -762,8 +762,9 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     const int nown = (B > wg) ? (B - 1 - wg) / nwg + 1 : 0;
     constexpr int HJ = 16;                                     // 16-byte pieces per lane and row
     const int hpc = p.d / 8;                                   // pieces per row
-    const bool fast_hd = (p.d % 8) == 0 && hpc <= 64 * HJ && p.d <= int(sizeof(lds_u) / sizeof(float)) &&
-                         (reinterpret_cast<uintptr_t>(h) & 15) == 0;
+    // (d = 0, where h may be null and every dot is 0, takes the generic loop, which reads nothing)
+    const bool fast_hd = p.d > 0 && (p.d % 8) == 0 && hpc <= 64 * HJ &&
+                         p.d <= int(sizeof(lds_u) / sizeof(float)) && (reinterpret_cast<uintptr_t>(h) & 15) == 0;
     if (fast_hd) {
       float* wl = reinterpret_cast<float*>(lds_u);
       for (int i = tid; i < p.d; i += NT) wl[i] = p.conf_w[i];

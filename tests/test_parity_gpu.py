@@ -97,6 +97,8 @@ SMALL = [
     dict(B=5, gamma=6, V=2051, r=128, d=8, dtype="bf16"),
     dict(B=9, gamma=4, V=777, r=16, d=20, dtype="f32"),
     dict(B=33, gamma=3, V=3000, r=64, d=40, dtype="f32"),
+    dict(B=20, gamma=3, V=3000, r=64, d=0, dtype="bf16"),              # no hidden state (d = 0)
+    dict(B=140, gamma=3, V=69632, r=256, d=0, dtype="bf16"),           # whole-tile kernel, d = 0
 ]
 
 

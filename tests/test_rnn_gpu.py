@@ -48,6 +48,7 @@ CASES = [
     (3, 64, 2048, 32, 16, "greedy"),          # the longest block (gamma = 64): 63 state steps
     (256, 2, 151936, 256, 32, "gumbel"),      # whole-tile kernel, two full groups, Gumbel-max
     (17, 3, 69648, 64, 16, "greedy"),         # whole-tile kernel, rank 64, ragged single group
+    (140, 3, 69632, 256, 0, "greedy"),        # whole-tile kernel without a hidden state (d = 0)
 ]
 
 
