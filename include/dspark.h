@@ -228,6 +228,25 @@ dspark_status dspark_rnn_draft(
     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dspark_gumbel_from_words — the Gumbel noise of the drafting kernels
+ * (dspark_markov_draft, dspark_rnn_draft, dspark_parallel_draft in
+ * DSPARK_GUMBEL mode) for given 32-bit hash words, computed by the same
+ * device function: out[i] = -ln(-ln u), u = (2 * (words[i] >> 9) + 1) * 2^-24.
+ *
+ * Defined by: Gumbel-max sampling from softmax(z_k) (the reading of the
+ * drafting distribution of [P-blog] §4, whose formula the pages lose); the
+ * words themselves come from the Philox4x32-10 counter layout documented at
+ * dspark_markov_draft.  For checking the noise arithmetic on its own.
+ *
+ * Arguments
+ *   n             number of words (0 is a no-op)
+ *   words  uint32 [n]   device, 4-byte aligned
+ *   out    fp32   [n] out device, 4-byte aligned
+ * Errors: DSPARK_ERR_INVALID_ARG for n < 0 or null / misaligned arrays.
+ */
+dspark_status dspark_gumbel_from_words(int n, const uint32_t* words, float* out, hipStream_t stream);
+
+/*
  * dspark_parallel_draft — drafting with the parallel stage alone: the
  * baseline without a sequential head, for measuring what the Markov head
  * adds to the drafting time.

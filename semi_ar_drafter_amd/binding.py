@@ -48,6 +48,8 @@ def _declare(lib):
                                      c_vp, c_f, c_vp, c_int, c_u64,
                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]
     lib.dspark_rnn_draft.restype = c_int
+    lib.dspark_gumbel_from_words.argtypes = [c_int, c_vp, c_vp, c_vp]
+    lib.dspark_gumbel_from_words.restype = c_int
     lib.dspark_schedule.argtypes = [c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
     lib.dspark_schedule.restype = c_int
     lib.dspark_parallel_draft.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_int, c_u64, c_vp, c_vp, c_vp]
@@ -229,6 +231,19 @@ def rnn_draft(anchor, U, h, W1, W2, decay, conf_w, conf_b: float, sts_T, mode: s
         _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
     _check(st)
     return tokens, logit, conf, surv
+
+
+def gumbel_from_words(words, out=None):
+    """The drafting kernels' Gumbel noise for given hash words (int32 device
+    tensor holding the 32-bit words); returns fp32 of the same length."""
+    torch = _torch()
+    lib = load()
+    _need(words, "words", torch.int32)
+    n = words.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=words.device)
+    _check(lib.dspark_gumbel_from_words(n, _ptr(words), _ptr(out), _stream()))
+    return out
 
 
 def parallel_draft(U, mode: str = "greedy", seed: int = 0, out=None):

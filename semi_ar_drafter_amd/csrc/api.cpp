@@ -193,6 +193,18 @@ dspark_status dspark_parallel_draft(int B, int gamma, int V, dspark_dtype dtype,
   return DSPARK_OK;
 }
 
+dspark_status dspark_gumbel_from_words(int n, const uint32_t* words, float* out, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (n < 0) return fail(DSPARK_ERR_INVALID_ARG, "negative size");
+  if (n == 0) return DSPARK_OK;
+  if (!words || !out) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(words) % 4 || reinterpret_cast<uintptr_t>(out) % 4)
+    return fail(DSPARK_ERR_INVALID_ARG, "misaligned array");
+  hipError_t e = dspark::launch_gumbel_words(n, words, out, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return DSPARK_OK;
+}
+
 dspark_status dspark_schedule_threshold(int B, int gamma, const float* surv, float tau, int32_t* lens,
                                         int32_t* m_out, hipStream_t stream) {
   g_last_error[0] = '\0';

@@ -56,6 +56,7 @@ hipError_t launch_schedule_threshold(int B, int gamma, const float* surv, float 
 
 hipError_t launch_parallel_draft(int B, int gamma, int V, bool bf16, const void* U, bool gumbel, uint64_t seed,
                                  int32_t* tokens, float* logit, hipStream_t stream);
+hipError_t launch_gumbel_words(int n, const uint32_t* words, float* out, hipStream_t stream);
 
 // Sequential-temperature fit: limits of one workgroup's LDS histogram.
 constexpr int kMaxStsGrid = 4096;

@@ -165,7 +165,19 @@ __global__ __launch_bounds__(kPThreads) void parallel_draft_kernel(int gamma, in
   }
 }
 
+// The Gumbel sample of the drafting kernels for given 32-bit hash words.
+__global__ __launch_bounds__(256) void gumbel_words_kernel(int n, const uint32_t* __restrict__ words,
+                                                           float* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = gumbel_from_word(words[i]);
+}
+
 }  // namespace
+
+hipError_t launch_gumbel_words(int n, const uint32_t* words, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(gumbel_words_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, n, words, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_parallel_draft(int B, int gamma, int V, bool bf16, const void* U, bool gumbel, uint64_t seed,
                                  int32_t* tokens, float* logit, hipStream_t stream) {

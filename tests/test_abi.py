@@ -112,6 +112,14 @@ def test_rnn_workspace_size(lib):
     assert a % 256 == 0 and a >= m + 2 * 256 * 256 * 2
 
 
+def test_gumbel_from_words_validation(lib):
+    assert lib.dspark_gumbel_from_words(-1, P, P, NULL) == INVALID
+    assert lib.dspark_gumbel_from_words(4, NULL, P, NULL) == INVALID
+    assert lib.dspark_gumbel_from_words(4, P, NULL, NULL) == INVALID
+    assert lib.dspark_gumbel_from_words(4, ctypes.c_void_p(0x10002), P, NULL) == INVALID
+    assert lib.dspark_gumbel_from_words(0, NULL, NULL, NULL) == OK
+
+
 def test_workspace_size(lib):
     assert lib.dspark_draft_workspace_bytes(0, 16, 151936, 256) == 0
     a = lib.dspark_draft_workspace_bytes(256, 16, 151936, 256)
