@@ -372,7 +372,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
                      "kernel": "markov_draft_kernel (one launch per dspark_markov_draft call)",
-                     "algorithmic_bytes_per_launch": abytes, "launch_us": round(draft_avg * 1e3, 2)},
+                     "algorithmic_bytes_per_launch": abytes, "launch_us": round(draft_avg * 1e3, 2),
+                     "launch_us_p10_p50_p90": [round(float(np.percentile(draft_ms, q)) * 1e3, 2) for q in (10, 50, 90)]},
         "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
