@@ -950,12 +950,20 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       // contiguous in the state buffer) into the U ring, 16 bytes per lane,
       // with the gather (device scope: written by the rows' owners before
       // their arrival)
+      // Each wave takes the rows it updates (wave, wave + NW, ...) into its
+      // own part of the ring (its three U slots), row after row.
       if constexpr (RING_STATE) {
         if (k > 1) {
           const char* src = reinterpret_cast<const char*>(p.state + (size_t((k - 1) & 1) * B + g0) * R);
-          const int nbytes = rows * R * 2;
-          for (int i = wave; i * 1024 < nbytes; i += NW)
-            if (i * 1024 + lane * 16 < nbytes) load_lds16_dev(src + i * 1024 + lane * 16, lds_u + i * 256);
+          const int nrw = (rows > wave) ? (rows - 1 - wave) / NW + 1 : 0;   // this wave's rows
+          const int nbytes = nrw * R * 2;
+          char* region = reinterpret_cast<char*>(lds_u + wave * 3 * 768);
+          for (int i = 0; i * 1024 < nbytes; ++i) {
+            const int off = i * 1024 + lane * 16;
+            const int rr = off / (R * 2);
+            if (off < nbytes)
+              load_lds16_dev(src + size_t(wave + rr * NW) * (R * 2) + (off - rr * R * 2), region + i * 1024);
+          }
         }
       }
       // outputs of step k-1 for owned rows, overlapping the gather
@@ -971,7 +979,39 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       // token as its input, so its embedding half is taken now; then the
       // rows' states s_k = bf16(a s_{k-1} + e) replace e in LDS as the
       // B operand, and each row's owner publishes its state for step k + 1.
-      if constexpr (RNN) {
+      if constexpr (RING_STATE) {
+        // Whole-tile kernel: wave w owns rows w, w + NW, ... of the group;
+        // for each it first takes the embedding half of the confidence dot
+        // (owned requests), then replaces e by the state (program order
+        // within the wave: no workgroup barrier in between), then stages its
+        // first U tiles into its part of the ring, whose states it has read.
+        const int j_lo = (g0 > wg) ? (g0 - wg + nwg - 1) / nwg : 0;
+        constexpr int PPR = R / 4;                                 // 4-channel pieces per row
+        const uint64_t* region = reinterpret_cast<const uint64_t*>(lds_u + wave * 3 * 768);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(p.state + size_t(k & 1) * B * R);
+        for (int rr = 0; wave + rr * NW < rows; ++rr) {
+          const int row = wave + rr * NW;
+          const int b = g0 + row;
+          const bool owned = (b % nwg) == wg;
+          if (owned) {
+            double acc = 0.0;
+            for (int i = lane; i < R; i += 64) acc += double(lds_we[i]) * double(to_f32(lds_e[EL::at(row, i)]));
+            acc = wave_sum_f64(acc);
+            if (lane == 0) lds_ce[(b - wg) / nwg - j_lo] = acc;
+          }
+          for (int q = lane; q < PPR; q += 64) {
+            st_t* ep = lds_e + EL::at(row, 4 * q);
+            const uint64_t sp = (k > 1) ? region[rr * PPR + q] : 0ull;
+            const u32x2_t sv = rnn_step4(&lds_dec[4 * q], __builtin_bit_cast(u32x2_t, sp),
+                                         *reinterpret_cast<const u32x2_t*>(ep));
+            *reinterpret_cast<u32x2_t*>(ep) = sv;
+            if (owned) store_dev(dst + (size_t(b) * R + 4 * q) / 4, __builtin_bit_cast(uint64_t, sv));
+          }
+        }
+        lds_wait();   // the states have been read before the ring is refilled
+        if (nt > 0) work(k, g0, rows).prefetch(pf0, pf1, pf2);
+        __syncthreads();   // every row's state is in place (B operand) and the confidence halves are visible
+      } else if constexpr (RNN) {
         const int j_lo = (g0 > wg) ? (g0 - wg + nwg - 1) / nwg : 0;
         const int j_hi = (g0 + rows > wg) ? (g0 + rows - wg + nwg - 1) / nwg : 0;
         for (int j = j_lo + wave; j < j_hi; j += NW) {
@@ -982,10 +1022,10 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           if (lane == 0) lds_ce[j - j_lo] = acc;
         }
         __syncthreads();   // every wave has read e before the states replace it
-        // this thread's pieces (4 channels, 8 bytes) of the previous states
-        // s_{k-1}: from the U ring (whole-tile kernel) or from the state
-        // buffer, four in flight at a time (guarded kernel; device scope:
-        // written by the rows' owners before their arrival); s_0 = 0
+        // Guarded kernel: this thread's pieces (4 channels, 8 bytes) of the
+        // previous states s_{k-1} from the state buffer, four in flight at a
+        // time (device scope: written by the rows' owners before their
+        // arrival); s_0 = 0
         constexpr int PPR = R / 4;                                // pieces per row
         constexpr int SPT = (GR * PPR + NT - 1) / NT;             // pieces per thread
         constexpr int BATCH = SPT < 4 ? SPT : 4;
@@ -998,10 +1038,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           for (int u = 0; u < BATCH; ++u) {
             const int q = min(tid + (u0 + u) * NT, rows * PPR - 1);   // clamped: always a valid address
             const int row = q / PPR;
-            if constexpr (RING_STATE)
-              sprev[u] = (k > 1) ? reinterpret_cast<const uint64_t*>(lds_u)[q] : 0ull;
-            else
-              sprev[u] = (k > 1) ? load_dev(src + (size_t(g0 + row) * R + (q - row * PPR) * 4) / 4) : 0ull;
+            sprev[u] = (k > 1) ? load_dev(src + (size_t(g0 + row) * R + (q - row * PPR) * 4) / 4) : 0ull;
           }
 #pragma unroll
           for (int u = 0; u < BATCH; ++u) {
@@ -1018,8 +1055,6 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
           }
         }
         __syncthreads();
-        if constexpr (RING_STATE)   // the ring is free again: this unit's first U tiles
-          if (nt > 0) work(k, g0, rows).prefetch(pf0, pf1, pf2);
       }
 
       // 4. z = U_k + e W2 on MFMA, argmax in registers, per request tile
