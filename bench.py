@@ -373,7 +373,11 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
                      "kernel": "markov_draft_kernel (one launch per dspark_markov_draft call)",
                      "algorithmic_bytes_per_launch": abytes, "launch_us": round(draft_avg * 1e3, 2),
-                     "launch_us_p10_p50_p90": [round(float(np.percentile(draft_ms, q)) * 1e3, 2) for q in (10, 50, 90)]},
+                     "launch_us_p10_p50_p90": [round(float(np.percentile(draft_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+                     "u_stream_gbs": round(u_bytes / (draft_avg / 1e3) / 1e9, 1),
+                     "frac_of_measured_stream": round(achieved / (u_bytes / (par_us / 1e6) / 1e9), 4),
+                     "measured_stream_note": "the parallel-only draft kernel (a streaming read of U with an argmax) "
+                                             "on the same U, taken as the measured streaming-read rate"},
         "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
