@@ -173,10 +173,11 @@ dspark_status dspark_schedule(
 /*
  * dspark_verify — strict prefix-match verification of the scheduled drafts.
  *
- * Defined by: [P-news] opening (the target verifies the block in one pass;
- * accepted tokens stick, the first rejected token and everything after it
- * are dropped); [P-blog] §3 (the target verifies the scheduled prefix; the
- * next anchor is the target's bonus token).
+ * Defined by: [P-news] opening (the target checks the whole draft block in
+ * one forward pass and keeps the drafts up to the first disagreement; the
+ * disagreeing draft and all later ones are discarded); [P-blog] §3 (the
+ * target verifies the scheduled prefix; the next anchor is the target's
+ * bonus token).
  *
  *   accepted[b] = largest a <= lens[b] with tokens[b][j] == target[b][j] for all j < a
  *   bonus[b]    = target[b][accepted[b]]
@@ -198,7 +199,7 @@ dspark_status dspark_verify(
  * Defined by: [P-blog] §4 "Semi-Autoregressive Generation" (sequential stage:
  * the transition bias B_k(x_0, x_{<k}, x_k) may depend on the anchor and the
  * whole draft prefix; "Two instantiations of the sequential block", RNN head:
- * a recurrent state that accumulates the full prefix history within a
+ * its state carries information from every earlier position of the draft
  * block) and [P-blog] §5 (confidence head inputs: the hidden state and the
  * Markov embedding of the previous draft token).  The pages give no
  * equations for the RNN head; this library's reading is a per-channel

@@ -124,9 +124,8 @@ def bf16_round(x32: np.ndarray) -> np.ndarray:
 
 def rnn_state_step(s_prev_bits: np.ndarray, decay: np.ndarray, e_bits: np.ndarray) -> np.ndarray:
     """One step of the RNN head's recurrent state (reading of [P-blog] §4
-    "Two instantiations of the sequential block", RNN head: a recurrent state
-    that accumulates the whole prefix history within a block; the pages give
-    no equations).  Per rank channel j:
+    "Two instantiations of the sequential block", RNN head: its state carries
+    every earlier position of the draft block; the pages give no equations).  Per rank channel j:
 
         s_k[j] = bf16( fp32( fp32(a[j] * s_{k-1}[j]) + e_k[j] ) )
 
@@ -393,8 +392,9 @@ def serve(weights: dict, iters: list, anchor0, t_step, n_min: int, policy: str =
 # Verification
 # ----------------------------------------------------------------------------
 def verify(tokens, target, lens):
-    """Strict prefix match ([P-news] opening: accepted tokens stick, the first
-    rejected token and everything after it are dropped; [P-blog] §3: the
+    """Strict prefix match ([P-news] opening: the drafts are kept up to the
+    first one the target disagrees with, which is discarded together with all
+    later drafts; [P-blog] §3: the
     target verifies the scheduled prefix).
 
     accepted_b = number of leading scheduled drafts equal to the target's

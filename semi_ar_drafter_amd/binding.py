@@ -137,14 +137,29 @@ def workspace_bytes(B: int, gamma: int, V: int, r: int) -> int:
     return int(load().dspark_draft_workspace_bytes(B, gamma, V, r))
 
 
+def _workspace_key(kind: str, device_index: int, stream_handle: int):
+    """Cache key of a library-owned workspace: one per (kind, device, HIP
+    stream).  Calls enqueued on one stream run one after another, so they
+    may share a workspace; calls on different streams may overlap and must
+    not (their grid-barrier counters and arg-max slots would mix)."""
+    return (kind, int(device_index), int(stream_handle))
+
+
 def _workspace(nbytes: int, device, kind: str = "draft"):
+    """The cached workspace for the current stream of `device`, at least
+    `nbytes` long.  A new one is zero-filled on that same stream, so the fill
+    is ordered before the call that uses it; every completed call leaves it
+    zero-filled again."""
     torch = _torch()
-    key = (kind, device.index if device.index is not None else torch.cuda.current_device())
-    ws = _ws_cache.get(key)
-    if ws is None or ws.numel() < nbytes:
-        # zero-filled once; every completed call leaves it zero-filled again
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ws_cache[key] = ws
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    stream = torch.cuda.current_stream(index)
+    key = _workspace_key(kind, index, stream.cuda_stream)
+    with _lock:
+        ws = _ws_cache.get(key)
+        if ws is None or ws.numel() < nbytes:
+            with torch.cuda.stream(stream):
+                ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
     return ws
 
 
@@ -155,7 +170,11 @@ def markov_draft(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, mode: str =
 
     U [B, gamma, V], h [B, gamma, d], W1 [V, r], W2 [r, V] are all float32 or
     all bfloat16 device tensors; anchor int32 [B]; conf_w fp32 [d + r];
-    sts_T fp32 [gamma]."""
+    sts_T fp32 [gamma].  The call is enqueued on torch's current stream.
+    Without `workspace`, a library-owned workspace cached per (device,
+    stream) is used: calls on one stream share it, calls on different
+    streams get different ones.  A caller-supplied workspace (zero-filled
+    uint8, 256-byte aligned) must not be shared by calls that can overlap."""
     torch = _torch()
     lib = load()
     _need(U, "U")

@@ -249,3 +249,78 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         binding.load(str(tmp_path / "missing.so"))
+
+
+def test_workspace_cache_is_per_device_and_stream(monkeypatch):
+    """The binding's library-owned workspace is cached per (device, stream):
+    calls on one stream reuse it (growing it when a larger one is needed),
+    calls on another stream or device get their own, each zero-filled on the
+    stream that will use it.  Exercised with a stand-in for torch's device
+    API (no GPU needed)."""
+    import contextlib
+
+    class Stream:
+        def __init__(self, handle):
+            self.cuda_stream = handle
+
+    made = []
+
+    class Buf:
+        def __init__(self, n, device, stream):
+            self.n, self.device, self.stream = n, device, stream
+
+        def numel(self):
+            return self.n
+
+    class Cuda:
+        current = {0: Stream(0x100), 1: Stream(0x200)}
+        active = None
+
+        @staticmethod
+        def current_device():
+            return 0
+
+        @staticmethod
+        def current_stream(index=None):
+            return Cuda.current[0 if index is None else index]
+
+        @staticmethod
+        @contextlib.contextmanager
+        def stream(s):
+            prev, Cuda.active = Cuda.active, s
+            yield
+            Cuda.active = prev
+
+    class Device:
+        def __init__(self, index):
+            self.index = index
+
+    class Torch:
+        cuda = Cuda
+        uint8 = "uint8"
+
+        @staticmethod
+        def zeros(n, dtype=None, device=None):
+            assert Cuda.active is not None, "zero fill must be enqueued on the caller's stream"
+            b = Buf(n, device.index, Cuda.active.cuda_stream)
+            made.append(b)
+            return b
+
+    monkeypatch.setattr(binding, "_torch", lambda: Torch)
+    monkeypatch.setattr(binding, "_ws_cache", {})
+    d0, d1 = Device(0), Device(1)
+    a = binding._workspace(1000, d0)
+    assert a.stream == 0x100 and a.device == 0
+    assert binding._workspace(500, d0) is a                 # same stream: reused
+    big = binding._workspace(5000, d0)                      # larger: replaced on the same stream
+    assert big is not a and big.n == 5000 and big.stream == 0x100
+    assert binding._workspace(100, d0) is big
+    Cuda.current[0] = Stream(0x300)                         # another stream on device 0
+    c = binding._workspace(100, d0)
+    assert c is not big and c.stream == 0x300
+    e = binding._workspace(100, d1)                         # device 1's current stream
+    assert e.device == 1 and e.stream == 0x200
+    s = binding._workspace(100, d0, kind="sts")             # another kind, same stream
+    assert s is not c
+    assert len(made) == 5
+    assert binding._workspace_key("draft", 0, 0x100) != binding._workspace_key("draft", 0, 0x300)

@@ -49,9 +49,9 @@ def test_small_shapes_match_the_oracle_and_the_cooperative_launch(B, gamma, V, r
         assert np.array_equal(a, b)
 
 
-def test_full_size_step_sampled_rows():
-    """B=256, gamma=16, V=151936: every token equals the cooperative launch's;
-    sampled rows match the oracle."""
+def test_full_size_step_all_rows():
+    """B=256, gamma=16, V=151936: every token equals the cooperative launch's,
+    and every request matches the oracle."""
     from semi_ar_drafter_amd import set_draft_launch
     w = wl.make_workload(wl.WORKLOADS[3])
     dv = to_device(w)
@@ -63,7 +63,7 @@ def test_full_size_step_sampled_rows():
     for o in outs:
         for a, b in zip(o, ref):
             assert np.array_equal(a, b)
-    st = check_draft(w, outs[-1], rows=[0, 101, 255])
+    st = check_draft(w, outs[-1])
     assert st.ok(), st
 
 

@@ -1,6 +1,6 @@
 """Pins of the oracle's RNN sequential head (reading of "DSpark: DeepSeek's new
 speculative decoding work", §4 "Two instantiations of the sequential block",
-RNN head: a recurrent state accumulating the prefix history within a block).
+RNN head, whose state carries every earlier position of the draft block).
 
 The pages give no equations, so the reading (state s_k = bf16(fp32(a * s_{k-1})
 + W1[x_{k-1}]), s_0 = 0, bias = s_k W2) is checked here against what it must

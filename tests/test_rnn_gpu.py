@@ -94,14 +94,15 @@ def test_repeated_calls_are_identical():
         assert np.array_equal(x, y)
 
 
-def test_full_size_sampled_rows():
+def test_full_size_all_rows():
+    """The B=256, gamma=16, V=151936 configuration: every request's chain
+    against the RNN-head oracle."""
     cfg = wl.WORKLOADS[3]
     w = wl.make_workload(cfg)
     say(f"[case] rnn full size {cfg.name} B={cfg.B} gamma={cfg.gamma} V={cfg.V} r={cfg.r} d={cfg.d}")
     dv = to_device(w)
     out = gpu_rnn_draft(dv)
-    rows = np.array([0, 1, 97, 128, 200, 255])
-    st = check_draft(w, out, rows=rows, head="rnn")
+    st = check_draft(w, out, head="rnn")
     say(f"  replays={st.replays} mismatches={st.mismatches} dlogit={st.max_dlogit:.2e} dconf={st.max_dconf:.2e}")
     assert st.ok(), st
     del dv
