@@ -135,6 +135,37 @@ dspark_status dspark_markov_draft(
     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dspark_markov_draft_noalloc — dspark_markov_draft without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments (minus workspace / workspace_bytes), outputs, errors and
+ * limits as dspark_markov_draft; the kernels are the same.  The scratch
+ * memory comes from a static device array of DSPARK_NOALLOC_SCRATCH_BYTES
+ * per GPU, held by the library until the process ends.  Its device address
+ * is looked up on the first call on each device (that call also zero-fills
+ * it with a small kernel on `stream`); every completed call leaves it
+ * zero-filled again.  Nothing is allocated on any call.
+ *   - Shapes whose dspark_draft_workspace_bytes(B, gamma, V, r) exceeds
+ *     DSPARK_NOALLOC_SCRATCH_BYTES return DSPARK_ERR_UNSUPPORTED before
+ *     anything is enqueued (B = 256, gamma = 16 needs about 1.1 MiB).
+ *   - All calls on one GPU share its scratch: calls that can overlap (other
+ *     streams, threads or processes on the same device) race and must not
+ *     be issued; calls on one stream are ordered and safe.
+ *   - A call whose kernel could not synchronise (tokens all -1) leaves the
+ *     scratch dirty; the next call cleans it and also returns all -1, as a
+ *     dirty workspace does for dspark_markov_draft.
+ */
+#define DSPARK_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+dspark_status dspark_markov_draft_noalloc(
+    int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+    const int32_t* anchor, const void* U, const void* h, const void* W1, const void* W2,
+    const float* conf_w, float conf_b, const float* sts_T,
+    dspark_sampling mode, uint64_t seed,
+    int32_t* tokens, float* logit, float* conf, float* surv, hipStream_t stream);
+
+/*
  * dspark_schedule — hardware-aware prefix scheduler: per-request verify
  * lengths that maximise expected committed tokens per unit of verify-step
  * cost.

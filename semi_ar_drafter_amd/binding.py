@@ -41,6 +41,11 @@ def _declare(lib):
                                         c_vp, c_f, c_vp, c_int, c_u64,
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]
     lib.dspark_markov_draft.restype = c_int
+    lib.dspark_markov_draft_noalloc.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int,
+                                                c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                c_vp, c_f, c_vp, c_int, c_u64,
+                                                c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.dspark_markov_draft_noalloc.restype = c_int
     lib.dspark_rnn_draft_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
     lib.dspark_rnn_draft_workspace_bytes.restype = c_size
     lib.dspark_rnn_draft.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int,
@@ -206,6 +211,47 @@ def markov_draft(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, mode: str =
         DSPARK_GUMBEL if mode == "gumbel" else DSPARK_GREEDY, ctypes.c_uint64(seed & (2 ** 64 - 1)),
         _ptr(tokens), _ptr(logit), _ptr(conf), _ptr(surv),
         _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    _check(st)
+    return tokens, logit, conf, surv
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def markov_draft_noalloc(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, mode: str = "greedy",
+                         seed: int = 0, out=None):
+    """markov_draft through dspark_markov_draft_noalloc: the library's static
+    per-device scratch replaces the workspace (nothing is allocated by the
+    library; `out`, if given, must hold the four output tensors).  Calls
+    that can overlap on one device must not be issued."""
+    torch = _torch()
+    lib = load()
+    _need(U, "U")
+    B, gamma, V = U.shape
+    dev = U.device
+    dt = U.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("U must be float32 or bfloat16")
+    r = W1.shape[1]
+    d = h.shape[2]
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(h, "h", dt, (B, gamma, d), dev)
+    _need(W1, "W1", dt, (V, r), dev)
+    _need(W2, "W2", dt, (r, V), dev)
+    _need(conf_w, "conf_w", torch.float32, (d + r,), dev)
+    _need(sts_T, "sts_T", torch.float32, (gamma,), dev)
+    if out is None:
+        out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               torch.empty((B, gamma), dtype=torch.float32, device=dev))
+    tokens, logit, conf, surv = out
+    st = lib.dspark_markov_draft_noalloc(
+        B, gamma, V, r, d, DSPARK_BF16 if dt == torch.bfloat16 else DSPARK_F32,
+        _ptr(anchor), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2),
+        _ptr(conf_w), ctypes.c_float(conf_b), _ptr(sts_T),
+        DSPARK_GUMBEL if mode == "gumbel" else DSPARK_GREEDY, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+        _ptr(tokens), _ptr(logit), _ptr(conf), _ptr(surv), _stream())
     _check(st)
     return tokens, logit, conf, surv
 

@@ -79,7 +79,7 @@ dspark_status draft_impl(int B, int gamma, int V, int r, int d, dspark_dtype dty
                          const void* U, const void* h, const void* W1, const void* W2, const float* decay,
                          bool rnn, const float* conf_w, float conf_b, const float* sts_T, dspark_sampling mode,
                          uint64_t seed, int32_t* tokens, float* logit, float* conf, float* surv, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+                         size_t workspace_bytes, hipStream_t stream, bool noalloc = false) {
   g_last_error[0] = '\0';
   if (B < 0 || gamma < 0 || V < 0 || r < 0 || d < 0)
     return fail(DSPARK_ERR_INVALID_ARG, "negative size");
@@ -100,10 +100,16 @@ dspark_status draft_impl(int B, int gamma, int V, int r, int d, dspark_dtype dty
       (rnn && reinterpret_cast<uintptr_t>(decay) % 4))
     return fail(DSPARK_ERR_INVALID_ARG, "misaligned tensor (W1 needs 16-byte alignment)");
   const size_t need = rnn ? dspark_rnn_draft_workspace_bytes(B, gamma, V, r) : dspark_draft_workspace_bytes(B, gamma, V, r);
-  if (!workspace || workspace_bytes < need)
+  if (noalloc) {
+    // allocation-free entry point: the launcher takes the static per-device
+    // scratch in place of a workspace, once every check has passed
+    if (need > dspark::kNoAllocScratchBytes)
+      return fail(DSPARK_ERR_UNSUPPORTED, "shape needs more workspace than the 8 MiB static scratch");
+  } else if (!workspace || workspace_bytes < need)
     return fail(DSPARK_ERR_WORKSPACE, rnn ? "workspace missing or smaller than dspark_rnn_draft_workspace_bytes()"
                                           : "workspace missing or smaller than dspark_draft_workspace_bytes()");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(DSPARK_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (!noalloc && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(DSPARK_ERR_WORKSPACE, "workspace not 256-byte aligned");
 
   dspark::DraftArgs a;
   a.B = B;
@@ -130,6 +136,7 @@ dspark_status draft_impl(int B, int gamma, int V, int r, int d, dspark_dtype dty
   a.ws_bytes = workspace_bytes;
   a.exclusive = g_draft_launch.load() == DSPARK_LAUNCH_EXCLUSIVE;
   a.decay = rnn ? decay : nullptr;
+  a.noalloc = noalloc;
   const char* why = nullptr;
   hipError_t e = dspark::launch_markov_draft(a, stream, &why);
   if (why) return fail(DSPARK_ERR_UNSUPPORTED, "%s", why);
@@ -147,6 +154,15 @@ dspark_status dspark_markov_draft(int B, int gamma, int V, int r, int d, dspark_
                                   hipStream_t stream) {
   return draft_impl(B, gamma, V, r, d, dtype, anchor, U, h, W1, W2, nullptr, false, conf_w, conf_b, sts_T, mode, seed,
                     tokens, logit, conf, surv, workspace, workspace_bytes, stream);
+}
+
+dspark_status dspark_markov_draft_noalloc(int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+                                          const int32_t* anchor, const void* U, const void* h, const void* W1,
+                                          const void* W2, const float* conf_w, float conf_b, const float* sts_T,
+                                          dspark_sampling mode, uint64_t seed, int32_t* tokens, float* logit,
+                                          float* conf, float* surv, hipStream_t stream) {
+  return draft_impl(B, gamma, V, r, d, dtype, anchor, U, h, W1, W2, nullptr, false, conf_w, conf_b, sts_T, mode, seed,
+                    tokens, logit, conf, surv, nullptr, 0, stream, /*noalloc=*/true);
 }
 
 dspark_status dspark_rnn_draft(int B, int gamma, int V, int r, int d, dspark_dtype dtype, const int32_t* anchor,

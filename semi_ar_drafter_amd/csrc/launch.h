@@ -34,6 +34,7 @@ struct DraftArgs {
   size_t ws_bytes;
   bool exclusive;   // plain launch: the caller guarantees nothing else runs on the device
   const float* decay = nullptr;   // non-null: RNN head with this per-channel state decay [r] (bf16 only)
+  bool noalloc = false;           // ws ignored: the per-device static scratch is used (Markov head)
 };
 
 // Workspace carve-up of the draft call (byte offsets, 256-aligned).
@@ -46,6 +47,12 @@ DraftWorkspace draft_workspace_layout(int B, int gamma, int r_state);
 // Returns hipSuccess or the first HIP error; sets *unsupported (with a reason)
 // when the shape is outside what the kernels handle.
 hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported);
+
+// Allocation-free draft entry point: size of the per-device static scratch
+// that replaces the caller's workspace, and its device address (set up and
+// zero-filled on `stream` at the first call on the current device).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
 
 hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min,
                            int n_count, int32_t* lens, int32_t* m_out, double* objective,

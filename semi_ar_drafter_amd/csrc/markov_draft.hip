@@ -35,6 +35,7 @@
 #include "device_util.h"
 #include "launch.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace dspark {
@@ -1190,6 +1191,19 @@ bool pick(bool bf16, int r, bool full, bool rnn, KernelChoice* out) {
   }
 }
 
+// Scratch of the allocation-free entry point (dspark_markov_draft_noalloc):
+// the draft workspace as a file-scope device array, one copy per GPU for the
+// life of the process.  Host code never passes `scratch` itself to a kernel
+// (its host-side name is not a device address); it takes the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+
+// Zero-fill of the scratch at its set-up (a kernel, not a memset node).
+__global__ __launch_bounds__(256) void scratch_clear_kernel(u32x4_t* p, size_t n16) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
 struct DeviceInfo {
   int cus = 0;
 };
@@ -1271,6 +1285,16 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   }
   const DraftWorkspace L = draft_workspace_layout(a.B, a.gamma, rnn ? a.r : 0);
   char* ws = static_cast<char*>(a.ws);
+  if (a.noalloc) {   // every check has passed: set up (first call) and take this device's scratch
+    if (rnn || L.total > kNoAllocScratchBytes) {
+      *unsupported = "shape needs more workspace than the static scratch";
+      return hipSuccess;
+    }
+    void* sp = nullptr;
+    e = noalloc_scratch(stream, &sp);
+    if (e != hipSuccess) return e;
+    ws = static_cast<char*>(sp);
+  }
   DraftParams p;
   p.B = a.B;
   p.gamma = a.gamma;
@@ -1314,6 +1338,35 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   void* args[] = {&p};
   if (a.exclusive) return hipLaunchKernel(kc.fn, dim3(nwg), dim3(kc.threads), args, 0, stream);
   return hipLaunchCooperativeKernel(kc.fn, dim3(nwg), dim3(kc.threads), args, 0, stream);
+}
+
+
+// Address of this device's scratch, set up on the first call per device:
+// hipGetSymbolAddress with the device current, then one zero-fill on
+// `stream` (ordered before the draft launch that follows on the same stream).
+// Later calls find the scratch zero-filled by the previous call's last phase.
+hipError_t noalloc_scratch(hipStream_t stream, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return hipErrorInvalidValue;
+    const size_t n16 = kNoAllocScratchBytes / 16;
+    scratch_clear_kernel<<<dim3(256), dim3(256), 0, stream>>>(static_cast<u32x4_t*>(p), n16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dspark
