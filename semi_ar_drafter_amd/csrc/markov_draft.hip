@@ -200,16 +200,19 @@ __device__ __forceinline__ int part_of(int t, int n, int parts) {
 // 16 x 32).  With TPW odd the last slot is an ordinary 16-wide tile.  A wave
 // owning nt < TPW tiles (nt >= 2) fills its spare slots with exact copies of
 // columns it already holds: a spare pair slot repeats pair 0, a spare last
-// slot repeats the second half of the last real pair.  Returns the first of
-// the four consecutive columns (relative to the wave's first column) that lane
-// group q holds in tile slot t.  Along t the ids a lane sees never decrease
-// except for exact repeats, so a strict comparison in t order still picks the
-// lowest id among equal scores.
+// slot repeats the second half of the last real pair.  With TPW even (no
+// last slot) and nt odd, the pair slot after the last complete pair covers
+// the wave's last two tiles (its first half repeats the previous pair's
+// second half).  Returns the first of the four consecutive columns (relative
+// to the wave's first column) that lane group q holds in tile slot t.  Along
+// t the ids a lane sees never decrease except for exact repeats, so a strict
+// comparison in t order still picks the lowest id among equal scores.
 __device__ __forceinline__ int pair_col(int t, int q, int nt, int tpw) {
   const int rp = nt >> 1;   // complete pairs the wave owns
   if (t < (tpw & ~1)) {
     const int pr = t >> 1;
-    return (pr < rp ? 32 * pr : 0) + 8 * q + 4 * (t & 1);
+    const int base = pr < rp ? 32 * pr : ((tpw & 1) == 0 && (nt & 1) && pr == rp) ? 32 * rp - 16 : 0;
+    return base + 8 * q + 4 * (t & 1);
   }
   return (nt & 1) ? 32 * rp + 4 * q : 32 * (rp - 1) + 8 * q + 4;
 }
@@ -325,29 +328,46 @@ struct TileWork {
   // they complete before the asm block ends, so the slot can be refilled
   // right after.
   __device__ __forceinline__ void unstage(int s, int ahead, f32x4_t (&acc)[NTF]) const {
-    static_assert(NP == 2 && LONE, "staging reads written for two pairs and a last slot");
+    static_assert(NP == 2, "staging reads written for two pairs (and an optional last slot)");
     const uint32_t base = lds_addr(slot(s));
     const uint32_t a0 = base + rP0, a1 = base + rP1, a2 = base + rL;
     u32x4_t q0, q1;
-    u32x2_t ql;
+    u32x2_t ql = u32x2_t{0u, 0u};
+    if constexpr (LONE) {
 #define DSPARK_UNSTAGE(WAIT)                                                                  \
   asm volatile("s_waitcnt " WAIT "\n\tds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\t"        \
                "ds_read_b64 %2, %5\n\ts_waitcnt lgkmcnt(0)"                                  \
                : "=&v"(q0), "=&v"(q1), "=&v"(ql)                                            \
                : "v"(a0), "v"(a1), "v"(a2)                                                  \
                : "memory")
-    if (ahead >= 2)
-      DSPARK_UNSTAGE("vmcnt(6)");
-    else if (ahead == 1)
-      DSPARK_UNSTAGE("vmcnt(3)");
-    else
-      DSPARK_UNSTAGE("vmcnt(0)");
+      if (ahead >= 2)
+        DSPARK_UNSTAGE("vmcnt(6)");
+      else if (ahead == 1)
+        DSPARK_UNSTAGE("vmcnt(3)");
+      else
+        DSPARK_UNSTAGE("vmcnt(0)");
 #undef DSPARK_UNSTAGE
+    } else {
+#define DSPARK_UNSTAGE(WAIT)                                                                  \
+  asm volatile("s_waitcnt " WAIT "\n\tds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\t"        \
+               "s_waitcnt lgkmcnt(0)"                                                        \
+               : "=&v"(q0), "=&v"(q1)                                                        \
+               : "v"(a0), "v"(a1)                                                            \
+               : "memory")
+      if (ahead >= 2)
+        DSPARK_UNSTAGE("vmcnt(6)");
+      else if (ahead == 1)
+        DSPARK_UNSTAGE("vmcnt(3)");
+      else
+        DSPARK_UNSTAGE("vmcnt(0)");
+#undef DSPARK_UNSTAGE
+      (void)a2;
+    }
     acc[0] = f32x4_t{bf16_lo(q0.x), bf16_hi(q0.x), bf16_lo(q0.y), bf16_hi(q0.y)};
     acc[1] = f32x4_t{bf16_lo(q0.z), bf16_hi(q0.z), bf16_lo(q0.w), bf16_hi(q0.w)};
     acc[2] = f32x4_t{bf16_lo(q1.x), bf16_hi(q1.x), bf16_lo(q1.y), bf16_hi(q1.y)};
     acc[3] = f32x4_t{bf16_lo(q1.z), bf16_hi(q1.z), bf16_lo(q1.w), bf16_hi(q1.w)};
-    acc[4] = f32x4_t{bf16_lo(ql.x), bf16_hi(ql.x), bf16_lo(ql.y), bf16_hi(ql.y)};
+    if constexpr (LONE) acc[4] = f32x4_t{bf16_lo(ql.x), bf16_hi(ql.x), bf16_lo(ql.y), bf16_hi(ql.y)};
   }
 
   // CHECKED: one request tile from registers, then the loads of tile bt + 3 into the same buffer.
@@ -1159,10 +1179,17 @@ struct KernelChoice {
 constexpr int kDraftWaves = 8;
 
 template <bool BF16, int R, bool G, bool RNN>
-KernelChoice pick_r(bool full) {
+KernelChoice pick_r(bool full, int tiles_per_wave) {
   constexpr int NW = kDraftWaves, GR = kMaxGroupRows;
   constexpr int TPW = BF16 ? 5 : 4;
   if constexpr (BF16) {
+    // rank 256, Markov head: four tiles per wave when they cover the
+    // vocabulary (W2 then takes 128 instead of 160 registers per lane and no
+    // wave computes a fifth, repeated slot)
+    if constexpr (R == 256 && !RNN)
+      if (full && tiles_per_wave <= 4)
+        return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, 4, GR, G, true, RNN>),
+                            NW * 64, 4};
     if (full)
       return KernelChoice{reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, true, RNN>),
                           NW * 64, TPW};
@@ -1172,21 +1199,22 @@ KernelChoice pick_r(bool full) {
 }
 
 template <bool G>
-bool pick(bool bf16, int r, bool full, bool rnn, KernelChoice* out) {
+bool pick(bool bf16, int r, bool full, bool rnn, int tpw_need, KernelChoice* out) {
+  const int n = tpw_need;
   if (bf16) {
     switch (r) {
-      case 32: *out = rnn ? pick_r<true, 32, G, true>(full) : pick_r<true, 32, G, false>(full); return true;
-      case 64: *out = rnn ? pick_r<true, 64, G, true>(full) : pick_r<true, 64, G, false>(full); return true;
-      case 128: *out = rnn ? pick_r<true, 128, G, true>(full) : pick_r<true, 128, G, false>(full); return true;
-      case 256: *out = rnn ? pick_r<true, 256, G, true>(full) : pick_r<true, 256, G, false>(full); return true;
+      case 32: *out = rnn ? pick_r<true, 32, G, true>(full, n) : pick_r<true, 32, G, false>(full, n); return true;
+      case 64: *out = rnn ? pick_r<true, 64, G, true>(full, n) : pick_r<true, 64, G, false>(full, n); return true;
+      case 128: *out = rnn ? pick_r<true, 128, G, true>(full, n) : pick_r<true, 128, G, false>(full, n); return true;
+      case 256: *out = rnn ? pick_r<true, 256, G, true>(full, n) : pick_r<true, 256, G, false>(full, n); return true;
       default: return false;
     }
   }
   if (rnn) return false;
   switch (r) {
-    case 16: *out = pick_r<false, 16, G, false>(full); return true;
-    case 32: *out = pick_r<false, 32, G, false>(full); return true;
-    case 64: *out = pick_r<false, 64, G, false>(full); return true;
+    case 16: *out = pick_r<false, 16, G, false>(full, n); return true;
+    case 32: *out = pick_r<false, 32, G, false>(full, n); return true;
+    case 64: *out = pick_r<false, 64, G, false>(full, n); return true;
     default: return false;
   }
 }
@@ -1252,7 +1280,7 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   *unsupported = nullptr;
   KernelChoice kc;
   const bool rnn = a.decay != nullptr;
-  if (!(a.gumbel ? pick<true>(a.bf16, a.r, false, rnn, &kc) : pick<false>(a.bf16, a.r, false, rnn, &kc))) {
+  if (!(a.gumbel ? pick<true>(a.bf16, a.r, false, rnn, 0, &kc) : pick<false>(a.bf16, a.r, false, rnn, 0, &kc))) {
     *unsupported = rnn ? "the RNN head supports bf16 storage with r in {32, 64, 128, 256}"
                        : a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
                                 : "fp32 drafting supports r in {16, 32, 64}";
@@ -1267,13 +1295,14 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   if (nwg < 1) nwg = 1;
   // the pair layout needs at least two tiles in every wave's range
   const bool full = (a.V % 16) == 0 && (tiles / nwg) / kDraftWaves >= 2;
-  if (full) {
-    if (a.gumbel)
-      pick<true>(a.bf16, a.r, true, rnn, &kc);
-    else
-      pick<false>(a.bf16, a.r, true, rnn, &kc);
-  }
   const int per_wg = (tiles + nwg - 1) / nwg;
+  if (full) {
+    const int tpw_need = (per_wg + kDraftWaves - 1) / kDraftWaves;   // most tiles any wave owns
+    if (a.gumbel)
+      pick<true>(a.bf16, a.r, true, rnn, tpw_need, &kc);
+    else
+      pick<false>(a.bf16, a.r, true, rnn, tpw_need, &kc);
+  }
   const int nwaves = kc.threads / 64;
   if ((per_wg + nwaves - 1) / nwaves > kc.tpw) {
     *unsupported = "vocabulary too large to keep W2 on chip on this GPU";

@@ -123,11 +123,13 @@ def test_small_gumbel(shape):
 
 
 @pytest.mark.parametrize("V,sampling", [(70016, "greedy"), (100000, "greedy"), (131072, "greedy"),
-                                        (100000, "gumbel")])
+                                        (100000, "gumbel"), (140000, "greedy"), (140000, "gumbel")])
 def test_vocab_splits_of_the_whole_tile_path(V, sampling):
     """V % 16 == 0 and at least two tiles per wave: the branch-free path with
-    paired tiles.  On a 256-CU GPU these vocabularies give waves owning
-    {2, 3}, {3, 4} and exactly 4 tiles, so every spare-slot case is covered."""
+    paired tiles.  On a 256-CU GPU the first four vocabularies take the
+    four-slot kernel with waves owning {2, 3}, {3, 4} and exactly 4 tiles
+    (odd counts use the overlapping last pair), the last two the five-slot
+    kernel with waves owning {4, 5} tiles (spare last slot)."""
     cfg = wl.small_config(B=24, gamma=3, V=V, r=256, d=64, dtype="bf16", sampling=sampling)
     w = wl.make_workload(cfg)
     if sampling == "gumbel":
