@@ -46,22 +46,33 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
   return x;
 }
 
+// Three-input exclusive or in one gfx950 instruction (v_bitop3_b32 with the
+// truth table 0x96: the output bit is set when an odd number of inputs are).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64-bit
 // multiplies on counter words 0 and 2 with the result words crossed and
 // xor-ed with the key; the key advances by the Weyl constants between rounds.
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;   // key increments
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
+                                             uint32_t k1) {
+  const uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
+  const uint64_t p0 = uint64_t(m0) * c0, p1 = uint64_t(m1) * c2;   // one 32x32->64 multiply each
+  const uint32_t hi0 = uint32_t(p0 >> 32), lo0 = uint32_t(p0);
+  const uint32_t hi1 = uint32_t(p1 >> 32), lo1 = uint32_t(p1);
+  const uint32_t n0 = xor3(hi1, c1, k0);
+  const uint32_t n2 = xor3(hi0, c3, k1);
+  c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+}
 __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
                                               uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t m0 = 0xD2511F53u, m1 = 0xCD9E8D57u;
-    const uint64_t p0 = uint64_t(m0) * c0, p1 = uint64_t(m1) * c2;   // one 32x32->64 multiply each
-    const uint32_t hi0 = uint32_t(p0 >> 32), lo0 = uint32_t(p0);
-    const uint32_t hi1 = uint32_t(p1 >> 32), lo1 = uint32_t(p1);
-    uint32_t n0 = hi1 ^ c1 ^ k0;
-    uint32_t n2 = hi0 ^ c3 ^ k1;
-    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
+    philox_round(c0, c1, c2, c3, k0, k1);
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
   }
 }
 

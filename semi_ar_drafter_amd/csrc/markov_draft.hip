@@ -406,11 +406,40 @@ struct TileWork {
     int btile = -1;
     f32x4_t bsel = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t bzsel = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Gumbel noise of every slot first: the slots' generator calls are
+    // independent chains of dependent multiplies, evaluated side by side
+    // (whole-tile path) Gumbel noise of every slot first: the slots'
+    // generator calls are independent chains of dependent multiplies,
+    // advanced round by round side by side
+    f32x4_t g[NTF];
+    if constexpr (GUMBEL && !CHECKED) {
+      uint32_t w[NTF][4];
+#pragma unroll
+      for (int t = 0; t < NTF; ++t) {
+        w[t][0] = uint32_t(tile_id0(t)) >> 2;
+        w[t][1] = uint32_t(k);
+        w[t][2] = uint32_t(b);
+        w[t][3] = 0u;
+      }
+      uint32_t k0 = seed_lo, k1 = seed_hi;
+#pragma unroll
+      for (int r = 0; r < 10; ++r) {
+#pragma unroll
+        for (int t = 0; t < NTF; ++t) philox_round(w[t][0], w[t][1], w[t][2], w[t][3], k0, k1);
+        k0 += kPhiloxW0;
+        k1 += kPhiloxW1;
+      }
+#pragma unroll
+      for (int t = 0; t < NTF; ++t)
+        g[t] = f32x4_t{gumbel_from_word(w[t][0]), gumbel_from_word(w[t][1]), gumbel_from_word(w[t][2]),
+                       gumbel_from_word(w[t][3])};
+    }
 #pragma unroll
     for (int t = 0; t < NTF; ++t) {
       if (CHECKED && t >= nt) continue;
       f32x4_t s4 = acc[t];
-      if constexpr (GUMBEL) {
+      if constexpr (GUMBEL && !CHECKED) s4 += g[t];
+      if constexpr (GUMBEL && CHECKED) {
         uint32_t c0 = uint32_t(tile_id0(t)) >> 2, c1 = uint32_t(k), c2 = uint32_t(b), c3 = 0u;
         philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
         s4 += f32x4_t{gumbel_from_word(c0), gumbel_from_word(c1), gumbel_from_word(c2), gumbel_from_word(c3)};
