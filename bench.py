@@ -86,6 +86,28 @@ def measured_traffic():
         return None
 
 
+GUMBEL_PROFILE = os.path.join(ROOT, "profiles", "markov_draft_cfg4_gumbel.md")
+
+
+def profiled_valu_fraction():
+    """VALU and MFMA fractions of the draft kernel on the large-vocabulary
+    Gumbel-max workload, from the committed rocprofv3 counter summary, or
+    None if it is missing or was taken on other draft kernel sources."""
+    if not os.path.exists(GUMBEL_PROFILE):
+        return None
+    text = open(GUMBEL_PROFILE).read()
+    import re
+    sha = re.search(r"kernel_source_sha256: ([0-9a-f]+)", text)
+    valu = re.search(r"VALU fraction = .* = ([0-9.]+) %", text)
+    mfma = re.search(r"MFMA utilisation = .* = ([0-9.]+) %", text)
+    if not (sha and valu and mfma) or sha.group(1) != source_digest(DRAFT_SOURCES):
+        return None
+    return {"frac": round(float(valu.group(1)) / 100, 4), "mfma_busy_frac": round(float(mfma.group(1)) / 100, 4),
+            "definition": "4 x SQ_ACTIVE_INST_VALU (quad-cycles, summed over waves) / (busy cycles x 1024 SIMDs); "
+                          "two waves per SIMD, so up to 2",
+            "source": "profiles/markov_draft_cfg4_gumbel.md (rocprofv3 counters of the same kernel sources)"}
+
+
 def copy_calibration(nbytes: int, reps: int):
     """A plain device-to-device copy of known size, for scaling the HBM
     counters (each launch reads and writes `nbytes`)."""
@@ -438,19 +460,21 @@ def main():
         torch.cuda.synchronize()
         par_us = sum(a.elapsed_time(b) for a, b in pev) / len(pev) * 1e3
 
-        # The RNN sequential head on the same inputs, outside the timed step.
-        decay = dev(w["decay"])
-        r_out = tuple(torch.empty((B, g), dtype=t, device="cuda")
-                      for t in (torch.int32, torch.float32, torch.float32, torch.float32))
-        for _ in range(2):
-            rnn_draft(anchor, U, h, W1, W2, decay, conf_w, w["conf_b"], sts_T, mode=mode, seed=seed, out=r_out)
-        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for a, b in rev:
-            a.record()
-            rnn_draft(anchor, U, h, W1, W2, decay, conf_w, w["conf_b"], sts_T, mode=mode, seed=seed, out=r_out)
-            b.record()
-        torch.cuda.synchronize()
-        rnn_us = sum(a.elapsed_time(b) for a, b in rev) / len(rev) * 1e3
+        # The RNN sequential head on the same inputs, outside the timed step
+        # (the RNN head is built for bf16 storage).
+        if cfg.dtype == "bf16":
+            decay = dev(w["decay"])
+            r_out = tuple(torch.empty((B, g), dtype=t, device="cuda")
+                          for t in (torch.int32, torch.float32, torch.float32, torch.float32))
+            for _ in range(2):
+                rnn_draft(anchor, U, h, W1, W2, decay, conf_w, w["conf_b"], sts_T, mode=mode, seed=seed, out=r_out)
+            rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            for a, b in rev:
+                a.record()
+                rnn_draft(anchor, U, h, W1, W2, decay, conf_w, w["conf_b"], sts_T, mode=mode, seed=seed, out=r_out)
+                b.record()
+            torch.cuda.synchronize()
+            rnn_us = sum(a.elapsed_time(b) for a, b in rev) / len(rev) * 1e3
 
         # W2 cold: the draft call after a 512 MB stream has evicted W2 from the caches
         w2_cold_us = time_w2_cold(torch, lambda: markov_draft(anchor, U, h, W1, W2, conf_w, w["conf_b"], sts_T,
@@ -487,7 +511,8 @@ def main():
         "outputs_valid": outputs_valid,
         "draft_launch": {"mode": args.draft_launch, "note": launch_note},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if args.config == 3 else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
                      "kernel": "markov_draft_kernel (one launch per dspark_markov_draft call)",
                      "algorithmic_bytes_per_launch": abytes, "launch_us": round(draft_avg * 1e3, 2),
@@ -499,6 +524,10 @@ def main():
         "verify_us": round(verify_us, 2),
         "cpu_baseline": None,
     }
+    if args.config == 4:
+        valu = profiled_valu_fraction()
+        if valu is not None:
+            result["valu"] = valu
     if other_ms is not None:
         result["draft_launch"].update({f"{other}_ms_per_step": round(other_ms, 5),
                                        f"{other}_draft_us": round(other_draft_us, 2)})
