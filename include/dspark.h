@@ -194,12 +194,27 @@ dspark_status dspark_markov_draft_noalloc(
  *   lens      int32 [B] out
  *   m_out     int32 [1] out  M*
  *   objective fp64  [1] out  Phi(M*) / 2^32 (may be NULL)
- * Limits: B * gamma <= 16384 (one workgroup sorts in LDS), else
- * DSPARK_ERR_UNSUPPORTED.
+ *   workspace  NULL, or >= dspark_schedule_workspace_bytes(B, gamma) bytes,
+ *              256-byte aligned, zero-filled before its first use; every
+ *              call leaves it zero-filled again.  Calls sharing a workspace
+ *              must not overlap.
+ * With a workspace the call is one launch of about B*gamma/16 workgroups
+ * that rank the entries by comparison (no sort) and hand the scan, the
+ * divisions and the arg-max to the last workgroup to finish; without one, a
+ * single workgroup sorts in LDS (slower, no workspace).  Both give the same
+ * result bit for bit for survivals that are not NaN; rows need not be
+ * non-increasing for either.
+ * Errors: DSPARK_ERR_WORKSPACE for a workspace that is too small or
+ * misaligned.  Limits: B * gamma <= 16384, else DSPARK_ERR_UNSUPPORTED.
  */
 dspark_status dspark_schedule(
     int B, int gamma, const float* surv, const double* t_step, int n_min, int n_count,
-    int32_t* lens, int32_t* m_out, double* objective, hipStream_t stream);
+    int32_t* lens, int32_t* m_out, double* objective, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
+
+/* Bytes of workspace dspark_schedule needs (a multiple of 256); 0 for
+ * B*gamma == 0 or B*gamma > 16384.  Needs no GPU. */
+size_t dspark_schedule_workspace_bytes(int B, int gamma);
 
 /*
  * dspark_verify — strict prefix-match verification of the scheduled drafts.
@@ -406,11 +421,18 @@ dspark_status dspark_schedule_threshold(
  *   tokens, logit, conf, surv  [iters][B][gamma] out   draft outputs
  *   lens, accepted, bonus      int32 [iters][B] out
  *   m_out                      int32 [iters] out       scheduled drafts per iteration
- *   workspace                  as dspark_markov_draft (dspark_draft_workspace_bytes)
+ *   workspace                  >= dspark_serve_workspace_bytes(B, gamma, V, r) bytes, 256-byte
+ *                              aligned, zero-filled before its first use (left zero-filled):
+ *                              the drafting workspace, then the scheduler's
  * Every argument is checked before the first launch; a HIP error later
  * leaves the iterations before it enqueued.  Limits: those of
  * dspark_markov_draft, and B * gamma <= 16384 for the GLOBAL policies.
  */
+/* Bytes of workspace dspark_serve needs: dspark_draft_workspace_bytes plus
+ * dspark_schedule_workspace_bytes.  Returns 0 for B*gamma == 0.  Needs no
+ * GPU. */
+size_t dspark_serve_workspace_bytes(int B, int gamma, int V, int r);
+
 dspark_status dspark_serve(
     int iters, int B, int gamma, int V, int r, int d, dspark_dtype dtype,
     const int32_t* anchor0, const void* U, const void* h, const void* W1, const void* W2,

@@ -55,8 +55,12 @@ def _declare(lib):
     lib.dspark_rnn_draft.restype = c_int
     lib.dspark_gumbel_from_words.argtypes = [c_int, c_vp, c_vp, c_vp]
     lib.dspark_gumbel_from_words.restype = c_int
-    lib.dspark_schedule.argtypes = [c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp]
+    lib.dspark_schedule.argtypes = [c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]
     lib.dspark_schedule.restype = c_int
+    lib.dspark_schedule_workspace_bytes.argtypes = [c_int, c_int]
+    lib.dspark_schedule_workspace_bytes.restype = c_size
+    lib.dspark_serve_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+    lib.dspark_serve_workspace_bytes.restype = c_size
     lib.dspark_parallel_draft.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_int, c_u64, c_vp, c_vp, c_vp]
     lib.dspark_parallel_draft.restype = c_int
     lib.dspark_set_draft_launch.argtypes = [c_int]
@@ -424,8 +428,8 @@ def serve(anchor0, U, h, W1, W2, conf_w, conf_b: float, sts_T, target, t_step, n
                    surv=f(iters, B, gamma), lens=f(iters, B, dtype=torch.int32),
                    accepted=f(iters, B, dtype=torch.int32), bonus=f(iters, B, dtype=torch.int32),
                    m=f(iters, dtype=torch.int32))
-    nbytes = workspace_bytes(B, gamma, V, r)
-    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    nbytes = int(lib.dspark_serve_workspace_bytes(B, gamma, V, r))
+    ws = workspace if workspace is not None else _workspace(nbytes, dev, "serve")
     st = lib.dspark_serve(
         iters, B, gamma, V, r, d, DSPARK_BF16 if dt == torch.bfloat16 else DSPARK_F32,
         _ptr(anchor0), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2), _ptr(conf_w), ctypes.c_float(conf_b), _ptr(sts_T),
@@ -438,8 +442,17 @@ def serve(anchor0, U, h, W1, W2, conf_w, conf_b: float, sts_T, target, t_step, n
     return out
 
 
-def schedule(surv, t_step, n_min: int, out=None):
-    """Prefix scheduler; returns (lens int32 [B], m int32 [1], objective fp64 [1])."""
+def schedule_workspace_bytes(B: int, gamma: int) -> int:
+    return int(load().dspark_schedule_workspace_bytes(B, gamma))
+
+
+def schedule(surv, t_step, n_min: int, out=None, workspace=None, one_workgroup: bool = False):
+    """Prefix scheduler; returns (lens int32 [B], m int32 [1], objective fp64 [1]).
+
+    By default the multi-workgroup kernel runs on a library-owned workspace
+    (cached per device and stream, or `workspace`, whose first 256 bytes are
+    zero before the first call); `one_workgroup=True` passes no workspace and
+    runs the one-workgroup sorting kernel instead."""
     torch = _torch()
     lib = load()
     _need(surv, "surv", torch.float32)
@@ -451,8 +464,14 @@ def schedule(surv, t_step, n_min: int, out=None):
                torch.empty(1, dtype=torch.int32, device=dev),
                torch.empty(1, dtype=torch.float64, device=dev))
     lens, m, obj = out
+    if one_workgroup:
+        ws, nbytes = None, 0
+    else:
+        nbytes = schedule_workspace_bytes(B, gamma)
+        ws = workspace if workspace is not None else (_workspace(nbytes, dev, "schedule") if nbytes else None)
     st = lib.dspark_schedule(B, gamma, _ptr(surv), _ptr(t_step), int(n_min), int(t_step.numel()),
-                             _ptr(lens), _ptr(m), _ptr(obj), _stream())
+                             _ptr(lens), _ptr(m), _ptr(obj), _ptr(ws) if ws is not None else None,
+                             ws.numel() if ws is not None else 0, _stream())
     _check(st)
     return lens, m, obj
 

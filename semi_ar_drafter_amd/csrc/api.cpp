@@ -66,6 +66,12 @@ size_t dspark_draft_workspace_bytes(int B, int gamma, int V, int r) {
   return dspark::draft_workspace_layout(B, gamma, 0).total;
 }
 
+size_t dspark_serve_workspace_bytes(int B, int gamma, int V, int r) {
+  const size_t draft = dspark_draft_workspace_bytes(B, gamma, V, r);
+  if (draft == 0) return 0;
+  return draft + dspark::schedule_workspace_bytes(B, gamma);
+}
+
 size_t dspark_rnn_draft_workspace_bytes(int B, int gamma, int V, int r) {
   (void)V;
   if (B <= 0 || gamma <= 0 || r <= 0) return 0;
@@ -174,8 +180,14 @@ dspark_status dspark_rnn_draft(int B, int gamma, int V, int r, int d, dspark_dty
                     tokens, logit, conf, surv, workspace, workspace_bytes, stream);
 }
 
+size_t dspark_schedule_workspace_bytes(int B, int gamma) {
+  if (B < 0 || gamma < 0) return 0;
+  return dspark::schedule_workspace_bytes(B, gamma);
+}
+
 dspark_status dspark_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min, int n_count,
-                              int32_t* lens, int32_t* m_out, double* objective, hipStream_t stream) {
+                              int32_t* lens, int32_t* m_out, double* objective, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = '\0';
   if (B < 0 || gamma < 0 || n_count < 1) return fail(DSPARK_ERR_INVALID_ARG, "negative size or empty step-cost table");
   if (!t_step || !m_out || (B > 0 && (!lens || (gamma > 0 && !surv))))
@@ -184,7 +196,13 @@ dspark_status dspark_schedule(int B, int gamma, const float* surv, const double*
     return fail(DSPARK_ERR_INVALID_ARG, "step-cost table must cover n = B (n_min <= B <= n_min + n_count - 1)");
   if ((long long)B * gamma > dspark::kMaxScheduleItems)
     return fail(DSPARK_ERR_UNSUPPORTED, "B * gamma > 16384");
-  hipError_t e = dspark::launch_schedule(B, gamma, surv, t_step, n_min, n_count, lens, m_out, objective, stream);
+  if (workspace) {
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(DSPARK_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (workspace_bytes < dspark::schedule_workspace_bytes(B, gamma))
+      return fail(DSPARK_ERR_WORKSPACE, "workspace smaller than dspark_schedule_workspace_bytes(B, gamma)");
+  }
+  hipError_t e =
+      dspark::launch_schedule(B, gamma, surv, t_step, n_min, n_count, lens, m_out, objective, workspace, stream);
   if (e != hipSuccess) return hip_fail(e);
   return DSPARK_OK;
 }
@@ -253,6 +271,12 @@ dspark_status dspark_serve(int iters, int B, int gamma, int V, int r, int d, dsp
       return fail(DSPARK_ERR_INVALID_ARG, "step-cost table must cover n = B (n_min <= B <= n_min + n_count - 1)");
     if ((long long)B * gamma > dspark::kMaxScheduleItems) return fail(DSPARK_ERR_UNSUPPORTED, "B * gamma > 16384");
   }
+  // the draft's workspace first, the scheduler's after it
+  const size_t draft_bytes = dspark_draft_workspace_bytes(B, gamma, V, r);
+  const size_t sched_bytes = policy == DSPARK_POLICY_THRESHOLD ? 0 : dspark::schedule_workspace_bytes(B, gamma);
+  if (workspace && workspace_bytes >= draft_bytes && workspace_bytes - draft_bytes < sched_bytes)
+    return fail(DSPARK_ERR_WORKSPACE, "workspace smaller than dspark_serve_workspace_bytes(B, gamma, V, r)");
+  void* sched_ws = workspace ? static_cast<unsigned char*>(workspace) + draft_bytes : nullptr;
   const size_t elem = dtype == DSPARK_BF16 ? 2 : 4;
   const size_t bg = size_t(B) * size_t(gamma);
   for (int t = 0; t < iters; ++t) {
@@ -272,7 +296,7 @@ dspark_status dspark_serve(int iters, int B, int gamma, int V, int r, int d, dsp
     } else {
       const float* src = (policy == DSPARK_POLICY_GLOBAL_DELAYED2 && t >= 2) ? surv + size_t(t - 2) * bg : surv_t;
       e = dspark::launch_schedule(B, gamma, src, t_step, n_min, n_count, lens + size_t(t) * B, m_out + t, nullptr,
-                                  stream);
+                                  sched_ws, stream);
     }
     if (e != hipSuccess) return hip_fail(e);
     e = dspark::launch_verify(B, gamma, tokens + size_t(t) * bg, target + size_t(t) * bg + size_t(t) * B,

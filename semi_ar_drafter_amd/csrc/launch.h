@@ -54,9 +54,13 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
 constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
 hipError_t noalloc_scratch(hipStream_t stream, void** out);
 
-hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min,
-                           int n_count, int32_t* lens, int32_t* m_out, double* objective,
-                           hipStream_t stream);
+// Bytes of the multi-workgroup scheduler's workspace (0 for B*gamma == 0 or
+// above kMaxScheduleItems).
+size_t schedule_workspace_bytes(int B, int gamma);
+// workspace == nullptr: the one-workgroup kernel; else the multi-workgroup
+// kernel on a workspace of schedule_workspace_bytes(B, gamma) bytes.
+hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min, int n_count,
+                           int32_t* lens, int32_t* m_out, double* objective, void* workspace, hipStream_t stream);
 
 hipError_t launch_schedule_threshold(int B, int gamma, const float* surv, float tau, int32_t* lens, int32_t* m_out,
                                     hipStream_t stream);

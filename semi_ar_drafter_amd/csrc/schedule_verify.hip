@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedWaves = kSchedThreads / 64;
+constexpr int kPrefetchSteps = 4;   // step costs per thread held in registers across the sort
 
 // Sort key: ascending key order = descending survival, then ascending flat
 // index (request-major), so the first M keys are the scheduler's top M.
@@ -53,21 +54,48 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
   int n2 = 4;
   while (n2 < n) n2 <<= 1;
 
+  // The step costs this thread divides by, read before the sort so that
+  // their latency hides behind it.
+  const int m_max = min(n, n_min + n_count - 1 - B);
+  const int C = (m_max + kSchedThreads - 1) / kSchedThreads;
+  const int p0 = min(tid * C, m_max), p1 = min(p0 + C, m_max);
+  const double t0 = tid == 0 ? t_step[B - n_min] : 1.0;
+  double ts[kPrefetchSteps];
+#pragma unroll
+  for (int j = 0; j < kPrefetchSteps; ++j) ts[j] = (p0 + j < p1) ? t_step[B + p0 + j + 1 - n_min] : 1.0;
+
   // Sort the keys ascending.  Up to half the key array, a merge sort: runs
   // of 4 sorted in registers, then merge levels that ping-pong between the
-  // two halves of `keys`, each thread placing 4 outputs after a binary
-  // search for where its output range splits the two input runs (merge
-  // path).  Every level reads and writes the keys once; the bitonic network
-  // used for larger inputs passes over them once per stage.  Keys are
-  // distinct apart from the padding, so the order is the same either way.
+  // two halves of `keys`, each thread placing 4 outputs after a search for
+  // where its output range splits the two input runs (merge path).  Every
+  // level reads and writes the keys once; the bitonic network used for
+  // larger inputs passes over them once per stage.  Keys are distinct apart
+  // from the padding, so the order is the same either way.
+  //
+  // Survival rows are non-increasing by construction (the documented input),
+  // so each request's keys are usually in order already: if every row is
+  // (checked), runs of gamma keys are sorted and, with gamma a power of two,
+  // the merge starts at runs of gamma.
   const uint64_t* sorted = keys;
+  bool merged = false;   // the sorted keys are in one half of `keys`, the other half is free
   if (n2 <= kMaxScheduleItems / 2) {
+    merged = true;
     uint64_t* src = keys;
     uint64_t* dst = keys + kMaxScheduleItems / 2;
+    bool in_order = true;   // this thread's keys continue their rows in order
     for (int q = tid * 4; q < n2; q += kSchedThreads * 4) {
       uint64_t v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = (q + j < n) ? sched_key(surv[q + j], uint32_t(q + j)) : ~0ull;
+      // the next key of the same row (the first key of the next quad)
+      const bool cont = q + 4 < n && (q + 4) % gamma != 0;
+      const uint64_t nx = cont ? sched_key(surv[q + 4], uint32_t(q + 4)) : ~0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool same_row = q + j + 1 < n && (q + j + 1) % gamma != 0;
+        const uint64_t next = (j < 3) ? v[j + 1] : nx;
+        if (same_row && next < v[j]) in_order = false;
+      }
       auto cs = [](uint64_t& a, uint64_t& b) {
         const uint64_t lo = a < b ? a : b, hi = a < b ? b : a;
         a = lo;
@@ -81,15 +109,37 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
 #pragma unroll
       for (int j = 0; j < 4; ++j) src[q + j] = v[j];
     }
-    for (int L = 4; L < n2; L <<= 1) {
+    const bool rows_in_order = __syncthreads_and(in_order) != 0;
+    int L0 = 4;
+    if (rows_in_order && (gamma & (gamma - 1)) == 0 && gamma > 4) L0 = gamma < n2 ? gamma : n2;
+    for (int L = L0; L < n2; L <<= 1) {
       __syncthreads();
       for (int o = tid * 4; o < n2; o += kSchedThreads * 4) {
         const int base = o & ~(2 * L - 1);
         const int d = o - base;
         const uint64_t* A = src + base;
         const uint64_t* Bv = src + base + L;
-        // i = outputs before o that come from A: the first i with A[i] > B[d-1-i]
+        // i = outputs before o that come from A: the first i with A[i] > B[d-1-i],
+        // searched four ways at a time (three probes per round trip)
         int lo = d > L ? d - L : 0, hi = d < L ? d : L;
+        while (hi - lo > 3) {
+          const int step = (hi - lo) >> 2;
+          const int m1 = lo + step, m2 = lo + 2 * step, m3 = lo + 3 * step;
+          const bool g1 = A[m1] > Bv[d - 1 - m1];
+          const bool g2 = A[m2] > Bv[d - 1 - m2];
+          const bool g3 = A[m3] > Bv[d - 1 - m3];
+          if (g1) {
+            hi = m1;
+          } else if (g2) {
+            lo = m1 + 1;
+            hi = m2;
+          } else if (g3) {
+            lo = m2 + 1;
+            hi = m3;
+          } else {
+            lo = m3 + 1;
+          }
+        }
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
           if (A[mid] > Bv[d - 1 - mid])
@@ -98,10 +148,28 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
             lo = mid + 1;
         }
         int i = lo, j = d - lo;
+        // the next four candidates of each run in registers (past a run's
+        // end: the largest key, never taken before a real one)
+        uint64_t ra[4], rb[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const bool take_a = j >= L || (i < L && A[i] <= Bv[j]);
-          dst[o + t] = take_a ? A[i++] : Bv[j++];
+          ra[t] = (i + t < L) ? A[i + t] : ~0ull;
+          rb[t] = (j + t < L) ? Bv[j + t] : ~0ull;
+        }
+        int ia = 0, ib = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint64_t ka = ra[0], kb = rb[0];
+          const bool take_a = (j + ib >= L) || (i + ia < L && ka <= kb);
+          dst[o + t] = take_a ? ka : kb;
+          // shift the run that was taken
+          if (take_a) {
+            ra[0] = ra[1]; ra[1] = ra[2]; ra[2] = ra[3]; ra[3] = ~0ull;
+            ++ia;
+          } else {
+            rb[0] = rb[1]; rb[1] = rb[2]; rb[2] = rb[3]; rb[3] = ~0ull;
+            ++ib;
+          }
         }
       }
       uint64_t* tmp = src;
@@ -132,9 +200,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
   __syncthreads();
 
   // M ranges over 0..m_max; thread t scans positions [t*C, (t+1)*C).
-  const int m_max = min(n, n_min + n_count - 1 - B);
-  const int C = (m_max + kSchedThreads - 1) / kSchedThreads;
-  const int p0 = min(tid * C, m_max), p1 = min(p0 + C, m_max);
   long long local = 0;
   for (int p = p0; p < p1; ++p) local += gain_fixed(sorted[p]);
   // block exclusive scan of the per-thread sums
@@ -145,28 +210,39 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
     if (lane >= d) incl += o;
   }
   if (lane == 63) wave_tot[wave] = incl;
+  // the per-request counts of the last phase live in the free half of `keys`
+  int* counts = reinterpret_cast<int*>(keys + (sorted == keys ? kMaxScheduleItems / 2 : 0));
+  if (merged)
+    for (int b = tid; b < B; b += kSchedThreads) counts[b] = 0;
   __syncthreads();
-  long long before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_tot[w];
-  long long G = before + incl - local;   // sum of gains at positions < p0
+  long long before = (lane < wave) ? wave_tot[lane] : 0;   // lane < 16
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
+  long long G = __shfl(before, 0, 64) + incl - local;   // sum of gains at positions < p0
 
   const long long base = (long long)B << 32;
   double best = -INFINITY;
   int best_m = 0x7FFFFFFF;
   if (tid == 0) {
-    best = double(base) / t_step[B - n_min];
+    best = double(base) / t0;
     best_m = 0;
   }
   for (int p = p0; p < p1; ++p) {
     G += gain_fixed(sorted[p]);
     const int M = p + 1;
-    const double phi = double(base + G) / t_step[B + M - n_min];
+    const int k = p - p0;
+    double t = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPrefetchSteps; ++j)
+      if (k == j) t = ts[j];
+    if (k >= kPrefetchSteps) t = t_step[B + M - n_min];
+    const double phi = double(base + G) / t;
     if (phi > best) {
       best = phi;
       best_m = M;
     }
   }
-  // block arg-max: larger phi, then smaller M
+  // block arg-max: larger phi, then smaller M (a total order, M being distinct)
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     const double ob = __shfl_xor(best, m, 64);
@@ -181,29 +257,282 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
     red_m[wave] = best_m;
   }
   __syncthreads();
-  if (tid == 0) {
-    double bb = red_phi[0];
-    int bm = red_m[0];
-    for (int w = 1; w < kSchedWaves; ++w)
-      if (red_phi[w] > bb || (red_phi[w] == bb && red_m[w] < bm)) {
-        bb = red_phi[w];
-        bm = red_m[w];
+  if (wave == 0) {
+    double bb = lane < kSchedWaves ? red_phi[lane] : -INFINITY;
+    int bm = lane < kSchedWaves ? red_m[lane] : 0x7FFFFFFF;
+#pragma unroll
+    for (int m = kSchedWaves / 2; m >= 1; m >>= 1) {
+      const double ob = __shfl_xor(bb, m, 64);
+      const int om = __shfl_xor(bm, m, 64);
+      if (ob > bb || (ob == bb && om < bm)) {
+        bb = ob;
+        bm = om;
       }
-    s_mstar = bm;
-    s_tau = (bm < n) ? sorted[bm] : ~0ull;
-    m_out[0] = bm;
-    if (objective) objective[0] = bb / 4294967296.0;
+    }
+    if (lane == 0) {
+      s_mstar = bm;
+      s_tau = (bm < n) ? sorted[bm] : ~0ull;
+      m_out[0] = bm;
+      if (objective) objective[0] = bb / 4294967296.0;
+    }
   }
   __syncthreads();
-  const uint64_t tau = s_tau;
-  for (int b = tid; b < B; b += kSchedThreads) {
-    int cnt = 0;
-    for (int k = 0; k < gamma; ++k) {
-      const int i = b * gamma + k;
-      cnt += sched_key(surv[i], uint32_t(i)) < tau ? 1 : 0;
+  if (merged) {
+    // lens[b] = how many of the first M* sorted keys belong to request b
+    const int mstar = s_mstar;
+    for (int p = tid; p < mstar; p += kSchedThreads) atomicAdd(&counts[uint32_t(sorted[p]) / uint32_t(gamma)], 1);
+    __syncthreads();
+    for (int b = tid; b < B; b += kSchedThreads) lens[b] = counts[b];
+  } else {
+    const uint64_t tau = s_tau;
+    for (int b = tid; b < B; b += kSchedThreads) {
+      int cnt = 0;
+      for (int k = 0; k < gamma; ++k) {
+        const int i = b * gamma + k;
+        cnt += sched_key(surv[i], uint32_t(i)) < tau ? 1 : 0;
+      }
+      lens[b] = cnt;
     }
-    lens[b] = cnt;
   }
+}
+
+// Multi-workgroup scheduler.  No sort: the rank of a key is the number of
+// keys below it, and with every key distinct the ranks are a permutation, so
+// a key stored at its rank lands where a sort would put it.  Workgroup g
+// ranks keys g*K .. g*K + K - 1 against all n keys, which its threads hold
+// in registers (E per thread): per key, a wave compares against its 64*E
+// keys, and the ballot's population count is the wave's share of the rank.
+//
+// The compares are 32-bit.  A key is (h, i): h = ~ord(S) (high word), i =
+// the flat index; (h', i') < (h, i) iff h' < h, or h' == h and i' < i.
+// Threads hold entries in 64-entry blocks of consecutive i, and a
+// workgroup's K <= 64 keys all fall in one block c.  For an entry of a block
+// wholly below c (i' < i for every key), "less" is h' <= h, i.e. h' - 1 < h;
+// for an entry above c it is h' < h.  So each held entry is stored as h' - 1
+// or h' by its block, one unsigned compare per (key, entry) gives the rank
+// apart from ties inside block c, and those are added per key from a ballot
+// of h' == h over block c masked to the lanes i' < i.  Exact for every
+// survival that is not NaN (h then lies in [2^23 - 1, 2^32 - 2^23], so h' - 1
+// and the padding value 2^32 - 1 stay in range).
+// Each workgroup stores its keys at their ranks, each beside the step cost
+// t_step[B + rank + 1 - n_min] that the division at M = rank + 1 needs,
+// then takes a ticket; the workgroup that draws the last ticket has the
+// whole sorted array visible, and does the rest as the one-workgroup kernel:
+// the scan of gains, one fp64 division per M, the arg-max, and per-request
+// counts of the first M* sorted keys (LDS counters).
+//
+// The last workgroup's thread t takes the Q = ceil(n / T) consecutive ranks
+// t*Q .. t*Q + Q - 1, so the sorted array is stored transposed (rank r at
+// entry (r % Q) * T + r / Q) and that workgroup's j-th load is contiguous
+// across threads.  Tickets are taken in two levels (per group of
+// workgroups, then per group) so that no counter sees more than a few dozen
+// atomics at once; the last workgroup puts every counter back to zero, so a
+// workspace whose first kRankHeader bytes start zero has them zero again
+// after each call.
+constexpr int kRankThreads = 512;
+constexpr int kRankWaves = kRankThreads / 64;
+constexpr int kTicketGroups = 8;
+constexpr int kTicketStride = 32;   // counters 128 bytes apart
+constexpr size_t kRankHeader = 2048;
+static_assert((kTicketGroups + 1) * kTicketStride * 4 <= int(kRankHeader), "ticket counters fit the header");
+static_assert(kMaxScheduleItems <= 32 * kRankThreads, "at most 32 keys per thread (the largest instance)");
+
+struct RankEntry {
+  uint64_t key;
+  double t;   // t_step[B + rank + 1 - n_min] (1.0 past m_max)
+};
+
+// LDS bytes of the per-request counters: four 8-bit counters per word when a
+// count cannot pass 255 (gamma <= 255), else one per word (then B <= 64).
+__host__ __device__ inline int rank_counter_words(int B, int gamma) { return gamma <= 255 ? (B + 3) / 4 : B; }
+
+template <int E, int K>
+__global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(
+    int B, int gamma, const float* __restrict__ surv, const double* __restrict__ t_step, int n_min, int n_count,
+    int32_t* lens, int32_t* m_out, double* objective, unsigned int* tickets, RankEntry* sorted) {
+  static_assert((K & (K - 1)) == 0 && K >= 4 && K <= 64, "keys per workgroup: a power of two, one per lane");
+  extern __shared__ unsigned int counters[];
+  __shared__ int wcnt[K][kRankWaves];
+  __shared__ long long wave_tot[kRankWaves];
+  __shared__ double red_phi[kRankWaves];
+  __shared__ int red_m[kRankWaves];
+  __shared__ int s_last, s_mstar;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = B * gamma;
+  const int g0 = blockIdx.x * K;
+  const int m_max = min(n, n_min + n_count - 1 - B);
+  const int Q = (n + kRankThreads - 1) / kRankThreads;   // ranks per thread of the last workgroup, <= E
+
+  // every entry's high word, E per thread (entry j*T + tid in slot j),
+  // lowered by one in blocks wholly below this workgroup's block c0; past n
+  // the largest value.  Loads are unconditional (clamped index) so that they
+  // all issue before the first wait; n >= 1.
+  const int c0 = g0 & ~63;
+  uint32_t hw[E];
+  float sv[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) sv[j] = surv[min(j * kRankThreads + tid, n - 1)];
+  // this workgroup's keys, one per lane (past n: copies of the last key,
+  // ranked but never stored), and block c0, one entry per lane
+  const float kv = surv[min(g0 + (lane & (K - 1)), n - 1)];
+  const float cv = surv[min(c0 + lane, n - 1)];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int e = j * kRankThreads + tid;
+    const uint32_t below = (j * kRankThreads + wave * 64 + 64 <= c0) ? 1u : 0u;   // wave-uniform
+    hw[j] = e < n ? ~ord_f32(sv[j]) - below : ~0u;
+  }
+  const uint32_t hc = c0 + lane < n ? ~ord_f32(cv) : ~0u;
+  // KG keys at a time, so that their compares and counts interleave (KG * E
+  // compare masks live at once: at most 32, which keeps them in SGPRs)
+  constexpr int KG = E >= 32 ? 1 : E >= 16 ? 2 : 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += KG) {
+    uint32_t h[KG];
+    int cnt[KG];
+#pragma unroll
+    for (int u = 0; u < KG; ++u) {
+      h[u] = ~ord_f32(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(kv), k0 + u)));
+      // ties inside block c0 at lower flat index, counted once (by wave 0)
+      const int below_lanes = g0 + k0 + u - c0;   // in [0, 64)
+      cnt[u] = wave == 0 ? __popcll(__ballot(hc == h[u]) & ((1ull << below_lanes) - 1)) : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+#pragma unroll
+      for (int u = 0; u < KG; ++u) cnt[u] += __popcll(__ballot(hw[j] < h[u]));
+    int mine_cnt = cnt[0];
+#pragma unroll
+    for (int u = 1; u < KG; ++u)
+      if (lane == u) mine_cnt = cnt[u];
+    if (lane < KG) wcnt[k0 + lane][wave] = mine_cnt;
+  }
+  __syncthreads();
+  if (tid < K && g0 + tid < n) {
+    int rank = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) rank += wcnt[tid][w];
+    const double t = rank + 1 <= m_max ? t_step[B + rank + 1 - n_min] : 1.0;
+    RankEntry* slot = &sorted[(rank % Q) * kRankThreads + rank / Q];
+    store_dev(&slot->key, sched_key(kv, uint32_t(g0 + tid)));
+    store_dev(&slot->t, t);
+  }
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) {
+    const int G = gridDim.x, grp = blockIdx.x % kTicketGroups;
+    const unsigned int in_group = unsigned((G - grp + kTicketGroups - 1) / kTicketGroups);
+    const unsigned int groups = unsigned(min(G, kTicketGroups));
+    bool last = false;
+    if (__hip_atomic_fetch_add(&tickets[(1 + grp) * kTicketStride], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == in_group - 1)
+      last = __hip_atomic_fetch_add(&tickets[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // Every other workgroup's stores completed before its ticket: drop any
+  // stale copy of the sorted array from this L2 (an earlier call's), then
+  // read it with ordinary (coalesced, cached) loads.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  // The last workgroup: ranks [p0, p1) per thread, M = p + 1.
+  const int p0 = min(tid * Q, m_max), p1 = min(p0 + Q, m_max);
+  uint64_t kp[E];
+  double tv[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const RankEntry v = sorted[min(j, Q - 1) * kRankThreads + tid];
+    kp[j] = v.key;
+    tv[j] = v.t;
+  }
+  const double t0 = t_step[B - n_min];
+  const bool packed = gamma <= 255;
+  for (int w = tid; w < rank_counter_words(B, gamma); w += kRankThreads) counters[w] = 0u;
+  long long local = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j)
+    if (p0 + j < p1) local += gain_fixed(kp[j]);
+  long long incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  long long before = (lane < wave) ? wave_tot[lane] : 0;   // lane < kRankWaves
+#pragma unroll
+  for (int m = kRankWaves / 2; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
+  long long G = __shfl(before, 0, 64) + incl - local;   // sum of gains at ranks < p0
+
+  const long long base = (long long)B << 32;
+  double best = -INFINITY;
+  int best_m = 0x7FFFFFFF;
+  if (tid == 0) {
+    best = double(base) / t0;
+    best_m = 0;
+  }
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (p0 + j >= p1) break;
+    G += gain_fixed(kp[j]);
+    const double phi = double(base + G) / tv[j];
+    if (phi > best) {
+      best = phi;
+      best_m = p0 + j + 1;
+    }
+  }
+  // arg-max: larger phi, then smaller M (a total order, M being distinct)
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const double ob = __shfl_xor(best, m, 64);
+    const int om = __shfl_xor(best_m, m, 64);
+    if (ob > best || (ob == best && om < best_m)) {
+      best = ob;
+      best_m = om;
+    }
+  }
+  if (lane == 0) {
+    red_phi[wave] = best;
+    red_m[wave] = best_m;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    double bb = lane < kRankWaves ? red_phi[lane] : -INFINITY;
+    int bm = lane < kRankWaves ? red_m[lane] : 0x7FFFFFFF;
+#pragma unroll
+    for (int m = kRankWaves / 2; m >= 1; m >>= 1) {
+      const double ob = __shfl_xor(bb, m, 64);
+      const int om = __shfl_xor(bm, m, 64);
+      if (ob > bb || (ob == bb && om < bm)) {
+        bb = ob;
+        bm = om;
+      }
+    }
+    if (lane == 0) {
+      s_mstar = bm;
+      m_out[0] = bm;
+      if (objective) objective[0] = bb / 4294967296.0;
+    }
+    if (lane <= kTicketGroups) store_dev(&tickets[lane * kTicketStride], 0u);
+  }
+  __syncthreads();
+  // lens[b] = how many of the first M* sorted keys belong to request b
+  const int mstar = s_mstar;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (p0 + j >= min(p1, mstar)) break;
+    const uint32_t b = uint32_t(kp[j]) / uint32_t(gamma);
+    if (packed)
+      atomicAdd(&counters[b >> 2], 1u << (8 * (b & 3)));
+    else
+      atomicAdd(&counters[b], 1u);
+  }
+  __syncthreads();
+  for (int b = tid; b < B; b += kRankThreads)
+    lens[b] = packed ? int((counters[b >> 2] >> (8 * (b & 3))) & 255u) : int(counters[b]);
 }
 
 // One workgroup: a thread per request (looping for B > 1024) scans its
@@ -249,10 +578,44 @@ __global__ __launch_bounds__(256) void verify_kernel(int B, int gamma, const int
 
 }  // namespace
 
+size_t schedule_workspace_bytes(int B, int gamma) {
+  const size_t n = size_t(B) * size_t(gamma);
+  if (n == 0 || n > size_t(kMaxScheduleItems)) return 0;
+  const size_t q = (n + kRankThreads - 1) / kRankThreads;   // the transposed array: q rows of kRankThreads
+  return kRankHeader + q * kRankThreads * sizeof(RankEntry);
+}
+
 hipError_t launch_schedule(int B, int gamma, const float* surv, const double* t_step, int n_min, int n_count,
-                           int32_t* lens, int32_t* m_out, double* objective, hipStream_t stream) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, B, gamma, surv, t_step, n_min,
-                     n_count, lens, m_out, objective);
+                           int32_t* lens, int32_t* m_out, double* objective, void* workspace, hipStream_t stream) {
+  const int n = B * gamma;
+  if (!workspace || n == 0) {
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, B, gamma, surv, t_step, n_min,
+                       n_count, lens, m_out, objective);
+    return hipGetLastError();
+  }
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  auto* tickets = reinterpret_cast<unsigned int*>(ws);
+  auto* sorted = reinterpret_cast<RankEntry*>(ws + kRankHeader);
+  const size_t lds = sizeof(unsigned int) * size_t(rank_counter_words(B, gamma));
+  const int per = (n + kRankThreads - 1) / kRankThreads;   // keys per thread
+  // keys ranked per workgroup grow with n: fewer workgroups re-reading all n
+  // keys, at the price of a longer compare loop
+#define DSPARK_RANK_LAUNCH(E, K)                                                                              \
+  hipLaunchKernelGGL((schedule_rank_kernel<E, K>), dim3((n + K - 1) / K), dim3(kRankThreads), lds, stream, B, \
+                     gamma, surv, t_step, n_min, n_count, lens, m_out, objective, tickets, sorted)
+  if (per <= 1)
+    DSPARK_RANK_LAUNCH(1, 16);
+  else if (per <= 2)
+    DSPARK_RANK_LAUNCH(2, 16);
+  else if (per <= 4)
+    DSPARK_RANK_LAUNCH(4, 16);
+  else if (per <= 8)
+    DSPARK_RANK_LAUNCH(8, 16);
+  else if (per <= 16)
+    DSPARK_RANK_LAUNCH(16, 16);
+  else
+    DSPARK_RANK_LAUNCH(32, 64);
+#undef DSPARK_RANK_LAUNCH
   return hipGetLastError();
 }
 

@@ -127,8 +127,9 @@ def test_workspace_size(lib):
     assert a % 256 == 0 and b % 256 == 0 and b > a > 256 * 16 * 8
 
 
-def sched(lib, B=4, gamma=4, n_min=4, n_count=17, surv=P, t=P, lens=P, m=P):
-    return lib.dspark_schedule(B, gamma, surv, t, n_min, n_count, lens, m, NULL, NULL)
+def sched(lib, B=4, gamma=4, n_min=4, n_count=17, surv=P, t=P, lens=P, m=P, ws=NULL, ws_bytes=0):
+    return lib.dspark_schedule(B, gamma, surv, t, n_min, n_count, lens, m, NULL, ws, ctypes.c_size_t(ws_bytes),
+                               NULL)
 
 
 def test_schedule_validation(lib):
@@ -141,6 +142,22 @@ def test_schedule_validation(lib):
     assert sched(lib, lens=NULL) == INVALID
     assert sched(lib, m=NULL) == INVALID
     assert sched(lib, B=1025, gamma=16, n_min=1025, n_count=16401) == UNSUPPORTED
+    need = lib.dspark_schedule_workspace_bytes(4, 4)
+    assert sched(lib, ws=P, ws_bytes=need - 1) == WORKSPACE
+    assert sched(lib, ws=ctypes.c_void_p(0x10080), ws_bytes=need) == WORKSPACE
+    assert "workspace" in lib.dspark_last_error().decode()
+
+
+def test_schedule_workspace_size(lib):
+    ws = lib.dspark_schedule_workspace_bytes
+    assert ws(0, 16) == 0 and ws(16, 0) == 0 and ws(-1, 4) == 0 and ws(1025, 16) == 0
+    # a 2 KiB block of ticket counters, then 16 bytes (sort key, step cost)
+    # per entry, in whole rows of 512
+    assert ws(256, 16) == 2048 + 4096 * 16
+    assert ws(3, 5) == 2048 + 512 * 16 and ws(1024, 16) == 2048 + 16384 * 16
+    d = lib.dspark_draft_workspace_bytes(256, 16, 151936, 256)
+    assert lib.dspark_serve_workspace_bytes(256, 16, 151936, 256) == d + ws(256, 16)
+    assert lib.dspark_serve_workspace_bytes(0, 16, 151936, 256) == 0
 
 
 def test_verify_validation(lib):
@@ -205,7 +222,8 @@ def test_schedule_threshold_validation(lib):
 
 
 def test_serve_validation(lib):
-    ws_need = lib.dspark_draft_workspace_bytes(4, 4, 1024, 32)
+    ws_need = lib.dspark_serve_workspace_bytes(4, 4, 1024, 32)
+    draft_need = lib.dspark_draft_workspace_bytes(4, 4, 1024, 32)
 
     def serve(iters=3, B=4, g=4, V=1024, r=32, d=16, dt=1, policy=0, n_min=4, n_count=17, ws=P, ws_bytes=None,
               mode=0, **over):
@@ -228,6 +246,8 @@ def test_serve_validation(lib):
     # the draft arguments are checked by iteration 0 before anything is enqueued
     assert serve(anchor=NULL) == INVALID and serve(W1=ctypes.c_void_p(0x10008)) == INVALID
     assert serve(ws=NULL) == WORKSPACE and serve(ws_bytes=ws_need - 1) == WORKSPACE
+    assert serve(ws_bytes=draft_need) == WORKSPACE          # no room for the scheduler's part
+    assert serve(ws_bytes=draft_need - 1) == WORKSPACE
     assert serve(dt=5) == INVALID and serve(mode=4) == INVALID
     assert lib.dspark_last_error().decode() != ""
 

@@ -54,10 +54,12 @@ def run_case(w, rows=None):
     return d, out
 
 
-def gpu_schedule(d, surv_np):
+def gpu_schedule(d, surv_np, path="ranked", workspace=None):
+    """dspark_schedule with a workspace (the multi-workgroup ranking kernel)
+    or without one (the one-workgroup sorting kernel)."""
     from semi_ar_drafter_amd import schedule
     surv = torch.from_numpy(surv_np).to("cuda:0")
-    lens, m, obj = schedule(surv, d["t_step"], d["n_min"])
+    lens, m, obj = schedule(surv, d["t_step"], d["n_min"], workspace=workspace, one_workgroup=path == "one_workgroup")
     torch.cuda.synchronize()
     return lens.cpu().numpy(), int(m.cpu()[0]), float(obj.cpu()[0])
 
@@ -200,44 +202,79 @@ def _rand_surv(rng, B, g, mode):
     return S
 
 
+SCHED_PATHS = ["ranked", "one_workgroup"]
+
+
+@pytest.mark.parametrize("path", SCHED_PATHS)
 @pytest.mark.parametrize("B,g", [(1, 1), (3, 5), (64, 16), (256, 16), (512, 16), (1024, 16), (100, 3)])
 @pytest.mark.parametrize("mode", ["random", "ties", "saturated"])
-def test_schedule_parity(B, g, mode):
+def test_schedule_parity(B, g, mode, path):
     rng = np.random.default_rng(B * 131 + g * 7 + len(mode))
     S = _rand_surv(rng, B, g, mode)
     for table in ("linear", "quad"):
         n = np.arange(B, B + B * g + 1, dtype=np.float64)
         t = 1.0 + 0.01 * n if table == "linear" else 4.0 + 0.02 * n + 2e-5 * n * n
         d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=B)
-        lens, m, obj = gpu_schedule(d, S)
+        lens, m, obj = gpu_schedule(d, S, path)
         o_lens, o_m, o_obj = orc.schedule(S, t, B)
         assert m == o_m and (lens == o_lens).all() and obj == o_obj, (table, m, o_m)
 
 
-@pytest.mark.parametrize("B,g", [(7, 5), (256, 16), (512, 16), (333, 21), (1024, 16)])
-def test_schedule_parity_rows_not_monotone(B, g):
-    """The sort inside the scheduler is a full sort: survivals in any order
-    (outside the documented contract) still give the oracle's top-M set."""
+@pytest.mark.parametrize("path", SCHED_PATHS)
+@pytest.mark.parametrize("B,g", [(7, 5), (256, 16), (512, 16), (333, 21), (1024, 16), (3000, 5)])
+def test_schedule_parity_rows_not_monotone(B, g, path):
+    """Both kernels order all entries (a full sort, or ranks over all
+    entries): survivals in any order (outside the documented contract)
+    still give the oracle's top-M set."""
     rng = np.random.default_rng(B * 7 + g)
     S = rng.random((B, g)).astype(np.float32)
     S[rng.random((B, g)) < 0.1] = np.float32(0.5)
     n = np.arange(B, B + B * g + 1, dtype=np.float64)
     t = 4.0 + 0.02 * n + 2e-5 * n * n
     d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=B)
-    lens, m, obj = gpu_schedule(d, S)
+    lens, m, obj = gpu_schedule(d, S, path)
     o_lens, o_m, o_obj = orc.schedule(S, t, B)
     assert m == o_m and (lens == o_lens).all() and obj == o_obj
 
 
-def test_schedule_table_offset_and_short_table():
+@pytest.mark.parametrize("path", SCHED_PATHS)
+def test_schedule_table_offset_and_short_table(path):
     rng = np.random.default_rng(3)
     S = _rand_surv(rng, 40, 8, "random")
     n_min = 10
     t = 2.0 + 0.05 * np.arange(n_min, 40 + 100, dtype=np.float64)   # covers M <= 99 only
     d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=n_min)
-    lens, m, obj = gpu_schedule(d, S)
+    lens, m, obj = gpu_schedule(d, S, path)
     o_lens, o_m, o_obj = orc.schedule(S, t, n_min)
     assert m == o_m and (lens == o_lens).all() and obj == o_obj
+
+
+def test_schedule_workspace_reused_across_shapes():
+    """One workspace, consecutive calls of different sizes: each call puts the
+    ticket counter back to zero, so every call's last workgroup is the one
+    that sees all ranks."""
+    from semi_ar_drafter_amd import binding
+    ws = torch.zeros(binding.schedule_workspace_bytes(1024, 16), dtype=torch.uint8, device="cuda:0")
+    rng = np.random.default_rng(21)
+    for B, g in [(1024, 16), (5, 3), (256, 16), (1, 1), (700, 7), (1024, 16)]:
+        S = _rand_surv(rng, B, g, "random")
+        t = 4.0 + 0.02 * np.arange(B, B + B * g + 1, dtype=np.float64) + 1e-5 * np.arange(B * g + 1) ** 2
+        d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=B)
+        lens, m, obj = gpu_schedule(d, S, "ranked", workspace=ws)
+        o_lens, o_m, o_obj = orc.schedule(S, t, B)
+        assert m == o_m and (lens == o_lens).all() and obj == o_obj, (B, g)
+    assert int(ws[:4].view(torch.int32).cpu()[0]) == 0
+
+
+@pytest.mark.parametrize("path", SCHED_PATHS)
+def test_schedule_no_drafts(path):
+    """gamma = 0: nothing to schedule, M* = 0 and every length 0."""
+    S = np.zeros((6, 0), dtype=np.float32)
+    t = np.array([3.0, 3.5], dtype=np.float64)
+    d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=6)
+    lens, m, obj = gpu_schedule(d, S, path)
+    o_lens, o_m, o_obj = orc.schedule(S, t, 6)
+    assert m == o_m == 0 and (lens == o_lens).all() and (lens == 0).all() and obj == o_obj
 
 
 def test_verify_parity_random():
