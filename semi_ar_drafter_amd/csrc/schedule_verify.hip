@@ -561,6 +561,39 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_threshold_kernel(int B
   }
 }
 
+// Verify with one lane per position: request b takes a segment of S lanes
+// (S a power of two > gamma, S <= 64), lane k loads tokens[b][k] and
+// target[b][k] together, so every load of the call is in flight at once;
+// the accepted length is the first flagged lane of the segment's ballot
+// (k >= lens[b] or a mismatch, and k = gamma always), and the bonus token is
+// the target word that lane already holds.
+template <int S>
+__global__ __launch_bounds__(256) void verify_lanes_kernel(int B, int gamma, const int32_t* __restrict__ tokens,
+                                                           const int32_t* __restrict__ target,
+                                                           const int32_t* __restrict__ lens, int32_t* accepted,
+                                                           int32_t* bonus) {
+  const int gl = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int b = gl / S, k = gl % S;
+  const bool live = b < B && k <= gamma;
+  int32_t tg = 0, tk = 0, L = 0;
+  if (live) {
+    tg = target[size_t(b) * (gamma + 1) + k];
+    if (k < gamma) tk = tokens[size_t(b) * gamma + k];
+    L = min(max(int(lens[b]), 0), gamma);
+  }
+  const bool stop = live && (k >= L || tk != tg);
+  const uint64_t m = __ballot(stop);
+  const int seg = lane & ~(S - 1);
+  const uint64_t mine = (S == 64) ? m : (m >> seg) & ((1ull << S) - 1);
+  const int a = __builtin_ctzll(mine | (1ull << (S - 1)));   // k = gamma always stops, so a <= gamma for live b
+  const int32_t bon = __shfl(tg, seg + a, 64);
+  if (live && k == 0) {
+    accepted[b] = a;
+    bonus[b] = bon;
+  }
+}
+
 __global__ __launch_bounds__(256) void verify_kernel(int B, int gamma, const int32_t* __restrict__ tokens,
                                                      const int32_t* __restrict__ target,
                                                      const int32_t* __restrict__ lens, int32_t* accepted,
@@ -628,8 +661,37 @@ hipError_t launch_schedule_threshold(int B, int gamma, const float* surv, float 
 
 hipError_t launch_verify(int B, int gamma, const int32_t* tokens, const int32_t* target, const int32_t* lens,
                          int32_t* accepted, int32_t* bonus, hipStream_t stream) {
-  hipLaunchKernelGGL(verify_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, gamma, tokens, target, lens,
-                     accepted, bonus);
+  // lanes per request: the smallest power of two above gamma, up to a wave
+  int S = 4;
+  while (S <= gamma && S < 64) S <<= 1;
+  if (gamma >= 64 || size_t(B) * S > size_t(0x7FFFFFFF)) {
+    hipLaunchKernelGGL(verify_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, gamma, tokens, target, lens,
+                       accepted, bonus);
+    return hipGetLastError();
+  }
+  const dim3 grid(unsigned((size_t(B) * S + 255) / 256)), block(256);
+  switch (S) {
+    case 4:
+      hipLaunchKernelGGL(verify_lanes_kernel<4>, grid, block, 0, stream, B, gamma, tokens, target, lens, accepted,
+                         bonus);
+      break;
+    case 8:
+      hipLaunchKernelGGL(verify_lanes_kernel<8>, grid, block, 0, stream, B, gamma, tokens, target, lens, accepted,
+                         bonus);
+      break;
+    case 16:
+      hipLaunchKernelGGL(verify_lanes_kernel<16>, grid, block, 0, stream, B, gamma, tokens, target, lens, accepted,
+                         bonus);
+      break;
+    case 32:
+      hipLaunchKernelGGL(verify_lanes_kernel<32>, grid, block, 0, stream, B, gamma, tokens, target, lens, accepted,
+                         bonus);
+      break;
+    default:
+      hipLaunchKernelGGL(verify_lanes_kernel<64>, grid, block, 0, stream, B, gamma, tokens, target, lens, accepted,
+                         bonus);
+      break;
+  }
   return hipGetLastError();
 }
 

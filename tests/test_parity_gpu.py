@@ -279,13 +279,22 @@ def test_schedule_no_drafts(path):
 
 def test_verify_parity_random():
     rng = np.random.default_rng(9)
-    for B, g, V in [(1, 1, 2), (1000, 16, 3), (513, 7, 2), (64, 16, 5)]:
+    # gamma < 64 runs one lane per position (segments of 4..64 lanes), gamma >= 64 one thread per request
+    for B, g, V in [(1, 1, 2), (1000, 16, 3), (513, 7, 2), (64, 16, 5), (100, 0, 2), (50, 63, 2), (20, 64, 2),
+                    (10, 100, 2), (300, 31, 2), (70, 32, 2), (5, 3, 2), (4097, 16, 2)]:
         tok = rng.integers(0, V, size=(B, g)).astype(np.int32)
         tgt = rng.integers(0, V, size=(B, g + 1)).astype(np.int32)
         lens = rng.integers(-2, g + 3, size=B).astype(np.int32)     # out-of-range lengths are clamped
         acc, bonus = gpu_verify(tok, tgt, lens)
         o_acc, o_bonus = orc.verify(tok, tgt, np.clip(lens, 0, g))
         assert (acc == o_acc).all() and (bonus == o_bonus).all()
+        # drafts that mostly agree with the target: long accepted prefixes
+        tok2 = tgt[:, :g].copy()
+        flip = rng.random((B, g)) < 0.03
+        tok2[flip] = (tok2[flip] + 1) % V
+        acc, bonus = gpu_verify(tok2, tgt, lens)
+        o_acc, o_bonus = orc.verify(tok2, tgt, np.clip(lens, 0, g))
+        assert (acc == o_acc).all() and (bonus == o_bonus).all(), (B, g)
 
 
 # --------------------------------------------------------------------------
