@@ -17,7 +17,10 @@ Prints one JSON line.  `value` = drafted tokens per second of the whole step
 `config.draft_launch`); the step and draft times under the library's default
 cooperative launch are reported beside it (`draft_launch`).  The timed
 tokens are checked to lie in [0, V) (`outputs_valid`; exit status 3
-otherwise).  `schedule_us` / `verify_us` time those two calls alone.  `roofline` rates the draft kernel against HBM
+otherwise).  `schedule_us` / `verify_us` are the device time per call of those
+two calls alone (50 calls captured in a graph and replayed);
+`schedule_verify_timing` adds the per-call latency as the step issues them
+and the scheduler's one-workgroup (no workspace) kernel.  `roofline` rates the draft kernel against HBM
 bandwidth with its algorithmic bytes; `cpu_baseline` times the CPU oracle on
 a bounded sample of requests of the same workload; `ablation` times
 dspark_parallel_draft (drafting without the sequential head) on the same U,
@@ -302,6 +305,33 @@ def oracle_side_timings(w, single_thread_rows: int):
     return res
 
 
+def graph_us(fn, calls: int = 50, reps: int = 5) -> float:
+    """Device time per call of `fn` (a library call that allocates nothing):
+    `calls` calls captured in one graph, replayed `reps` times, median."""
+    import numpy as np
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / calls)
+    return float(np.median(ts))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,8 +361,8 @@ def main():
     import numpy as np
     import torch
 
-    from semi_ar_drafter_amd import (markov_draft, parallel_draft, rnn_draft, schedule, serve, set_draft_launch,
-                                     sts_fit, verify)
+    from semi_ar_drafter_amd import (markov_draft, parallel_draft, rnn_draft, schedule, schedule_workspace_bytes,
+                                     serve, set_draft_launch, sts_fit, verify)
     from semi_ar_drafter_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -428,7 +458,11 @@ def main():
         other_draft_us = sum(a.elapsed_time(b) for a, b in oev) / K * 1e3
         set_draft_launch(args.draft_launch)
 
-    # per-kernel latency of the scheduler and verify calls (events around each)
+    # Latency of the scheduler and verify calls: events around each call as
+    # the step issues it (includes the host-side launch of a small kernel),
+    # and the device time per call with 50 calls captured in a graph and
+    # replayed (launch overhead of the device alone; both kernels allocate
+    # nothing, clear nothing with memset and leave their workspace as found).
     sv = []
     for _ in range(20):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -439,8 +473,12 @@ def main():
         e[2].record()
         sv.append(e)
     torch.cuda.synchronize()
-    sched_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b, _ in sv]))
-    verify_us = float(np.median([b.elapsed_time(c) * 1e3 for _, b, c in sv]))
+    sched_call_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b, _ in sv]))
+    verify_call_us = float(np.median([b.elapsed_time(c) * 1e3 for _, b, c in sv]))
+    sched_ws = torch.zeros(schedule_workspace_bytes(B, g), dtype=torch.uint8, device="cuda")
+    sched_us = graph_us(lambda: schedule(outs[3], t_step, w["n_min"], out=sched_out, workspace=sched_ws))
+    sched_1wg_us = graph_us(lambda: schedule(outs[3], t_step, w["n_min"], out=sched_out, one_workgroup=True))
+    verify_us = graph_us(lambda: verify(outs[0], target, sched_out[0], out=ver_out))
 
     u_bytes = B * g * cfg.V * (2 if cfg.dtype == "bf16" else 4)
     par_us = rnn_us = w2_cold_us = None
@@ -522,6 +560,11 @@ def main():
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "schedule_us": round(sched_us, 2),
         "verify_us": round(verify_us, 2),
+        "schedule_verify_timing": {
+            "note": "schedule_us / verify_us: device time per call, 50 calls captured in a graph and replayed; "
+                    "*_call_us: events around one call as the step issues it (adds the host-side launch)",
+            "schedule_call_us": round(sched_call_us, 2), "verify_call_us": round(verify_call_us, 2),
+            "schedule_one_workgroup_us": round(sched_1wg_us, 2)},
         "cpu_baseline": None,
     }
     if args.config == 4:
