@@ -249,6 +249,23 @@ def test_schedule_table_offset_and_short_table(path):
     assert m == o_m and (lens == o_lens).all() and obj == o_obj
 
 
+@pytest.mark.parametrize("path", SCHED_PATHS)
+@pytest.mark.parametrize("B,g", [(1, 300), (3, 1000), (16, 1024), (16384, 1), (4096, 4), (2, 8192)])
+def test_schedule_extreme_shapes(B, g, path):
+    """Long rows (gamma > 255: one LDS counter per request instead of four
+    per word), the most requests (B = 16384), and a table shorter than the
+    drafts for the widest rows."""
+    rng = np.random.default_rng(B + 3 * g)
+    S = _rand_surv(rng, B, g, "random" if B % 2 else "ties")
+    n_all = B * g
+    cnt = min(n_all + 1, 5000) if g >= 1000 else n_all + 1
+    t = 4.0 + 0.02 * np.arange(B, B + cnt, dtype=np.float64) + 3e-6 * np.arange(cnt, dtype=np.float64) ** 2
+    d = dict(t_step=torch.from_numpy(t).to("cuda:0"), n_min=B)
+    lens, m, obj = gpu_schedule(d, S, path)
+    o_lens, o_m, o_obj = orc.schedule(S, t, B)
+    assert m == o_m and (lens == o_lens).all() and obj == o_obj, (B, g, m, o_m)
+
+
 def test_schedule_workspace_reused_across_shapes():
     """One workspace, consecutive calls of different sizes: each call puts the
     ticket counter back to zero, so every call's last workgroup is the one
