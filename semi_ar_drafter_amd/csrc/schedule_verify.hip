@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(
   __shared__ long long wave_tot[kRankWaves];
   __shared__ double red_phi[kRankWaves];
   __shared__ int red_m[kRankWaves];
-  __shared__ int s_last, s_mstar;
+  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = B * gamma;
@@ -507,28 +507,27 @@ __global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(
     red_m[wave] = best_m;
   }
   __syncthreads();
-  if (wave == 0) {
-    double bb = lane < kRankWaves ? red_phi[lane] : -INFINITY;
-    int bm = lane < kRankWaves ? red_m[lane] : 0x7FFFFFFF;
+  // every wave reduces the per-wave winners itself (no broadcast barrier)
+  double bb = lane < kRankWaves ? red_phi[lane] : -INFINITY;
+  int bm = lane < kRankWaves ? red_m[lane] : 0x7FFFFFFF;
 #pragma unroll
-    for (int m = kRankWaves / 2; m >= 1; m >>= 1) {
-      const double ob = __shfl_xor(bb, m, 64);
-      const int om = __shfl_xor(bm, m, 64);
-      if (ob > bb || (ob == bb && om < bm)) {
-        bb = ob;
-        bm = om;
-      }
+  for (int m = kRankWaves / 2; m >= 1; m >>= 1) {
+    const double ob = __shfl_xor(bb, m, 64);
+    const int om = __shfl_xor(bm, m, 64);
+    if (ob > bb || (ob == bb && om < bm)) {
+      bb = ob;
+      bm = om;
     }
+  }
+  const int mstar = __shfl(bm, 0, 64);
+  if (wave == 0) {
     if (lane == 0) {
-      s_mstar = bm;
       m_out[0] = bm;
       if (objective) objective[0] = bb / 4294967296.0;
     }
     if (lane <= kTicketGroups) store_dev(&tickets[lane * kTicketStride], 0u);
   }
-  __syncthreads();
   // lens[b] = how many of the first M* sorted keys belong to request b
-  const int mstar = s_mstar;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     if (p0 + j >= min(p1, mstar)) break;
