@@ -6,9 +6,17 @@
 // maximising (B + sum of scheduled survivals) / t_step(B + M).  Survival is
 // non-increasing along each request, so the best set of M drafts is the top
 // M by (S desc, request asc, position asc) and only M has to be searched.
-// One workgroup of 1024 threads: merge sort (bitonic above 8192 items) of
-// 64-bit keys in LDS, a block scan of fixed-point gains, one fp64 division per candidate M, a
-// block arg-max, and a per-request count below the M*-th key.
+// Two kernels give the same result bit for bit:
+//  * with a workspace (schedule_rank_kernel): every entry's rank counted by
+//    comparison across about B*gamma/16 workgroups, the keys stored at their
+//    ranks, and the last workgroup to finish does the scan of fixed-point
+//    gains, one fp64 division per candidate M, the arg-max and the
+//    per-request counts;
+//  * without one (schedule_kernel): one workgroup of 1024 threads sorts the
+//    64-bit keys in LDS (merge sort, bitonic above 8192 items), then the same
+//    scan, divisions, arg-max and counts.
+// Verify takes one lane per draft position (gamma < 64) or one thread per
+// request.
 //
 // Static-threshold scheduler (the baseline of "DSpark: DeepSeek's new
 // speculative decoding work", §6): each request verifies the longest prefix
