@@ -46,6 +46,51 @@ __device__ __forceinline__ long long gain_fixed(uint64_t key) {
   return (long long)rint(double(s) * 4294967296.0);
 }
 
+// Wave-wide scan and arg-max with DPP lane shifts (no LDS crossbar): row_shr
+// by 1, 2, 4 and 8 within each row of 16 lanes, then row_bcast:15 into rows
+// 1 and 3 and row_bcast:31 into rows 2 and 3.  Lanes whose source is outside
+// the row, or whose row is masked, receive the identity passed as `old`.
+template <int CTRL, int ROWM>
+__device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(x), CTRL, ROWM, 0xF, false));
+}
+template <int CTRL, int ROWM>
+__device__ __forceinline__ long long dpp_i64(long long v) {
+  const uint64_t u = uint64_t(v);
+  return (long long)((uint64_t(dpp32<CTRL, ROWM>(0u, uint32_t(u >> 32))) << 32) | dpp32<CTRL, ROWM>(0u, uint32_t(u)));
+}
+// inclusive prefix sum over the lanes of the wave
+__device__ __forceinline__ long long wave_scan_i64(long long v) {
+  v += dpp_i64<0x111, 0xF>(v);
+  v += dpp_i64<0x112, 0xF>(v);
+  v += dpp_i64<0x114, 0xF>(v);
+  v += dpp_i64<0x118, 0xF>(v);
+  v += dpp_i64<0x142, 0xA>(v);
+  v += dpp_i64<0x143, 0xC>(v);
+  return v;
+}
+template <int CTRL, int ROWM>
+__device__ __forceinline__ void dpp_argmax_step(double& b, int& m) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, b);
+  const uint32_t lo = dpp32<CTRL, ROWM>(0u, uint32_t(u));
+  const uint32_t hi = dpp32<CTRL, ROWM>(0xFFF00000u, uint32_t(u >> 32));   // -inf where no source
+  const int om = int(dpp32<CTRL, ROWM>(0x7FFFFFFFu, uint32_t(m)));
+  const double ob = __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+  if (ob > b || (ob == b && om < m)) {
+    b = ob;
+    m = om;
+  }
+}
+// larger value, then smaller index, over the wave; the result is in lane 63
+__device__ __forceinline__ void wave_argmax_to_lane63(double& b, int& m) {
+  dpp_argmax_step<0x111, 0xF>(b, m);
+  dpp_argmax_step<0x112, 0xF>(b, m);
+  dpp_argmax_step<0x114, 0xF>(b, m);
+  dpp_argmax_step<0x118, 0xF>(b, m);
+  dpp_argmax_step<0x142, 0xA>(b, m);
+  dpp_argmax_step<0x143, 0xC>(b, m);
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamma, const float* __restrict__ surv,
                                                                  const double* __restrict__ t_step, int n_min,
                                                                  int n_count, int32_t* lens, int32_t* m_out,
@@ -211,22 +256,18 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
   long long local = 0;
   for (int p = p0; p < p1; ++p) local += gain_fixed(sorted[p]);
   // block exclusive scan of the per-thread sums
-  long long incl = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const long long o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
+  const long long incl = wave_scan_i64(local);
   if (lane == 63) wave_tot[wave] = incl;
   // the per-request counts of the last phase live in the free half of `keys`
   int* counts = reinterpret_cast<int*>(keys + (sorted == keys ? kMaxScheduleItems / 2 : 0));
   if (merged)
     for (int b = tid; b < B; b += kSchedThreads) counts[b] = 0;
   __syncthreads();
-  long long before = (lane < wave) ? wave_tot[lane] : 0;   // lane < 16
+  long long before = 0;
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
-  long long G = __shfl(before, 0, 64) + incl - local;   // sum of gains at positions < p0
+  for (int w = 0; w < kSchedWaves; ++w)
+    if (w < wave) before += wave_tot[w];
+  long long G = before + incl - local;   // sum of gains at positions < p0
 
   const long long base = (long long)B << 32;
   double best = -INFINITY;
@@ -251,27 +292,19 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
     }
   }
   // block arg-max: larger phi, then smaller M (a total order, M being distinct)
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const double ob = __shfl_xor(best, m, 64);
-    const int om = __shfl_xor(best_m, m, 64);
-    if (ob > best || (ob == best && om < best_m)) {
-      best = ob;
-      best_m = om;
-    }
-  }
-  if (lane == 0) {
+  wave_argmax_to_lane63(best, best_m);
+  if (lane == 63) {
     red_phi[wave] = best;
     red_m[wave] = best_m;
   }
   __syncthreads();
   if (wave == 0) {
-    double bb = lane < kSchedWaves ? red_phi[lane] : -INFINITY;
-    int bm = lane < kSchedWaves ? red_m[lane] : 0x7FFFFFFF;
+    double bb = red_phi[0];
+    int bm = red_m[0];
 #pragma unroll
-    for (int m = kSchedWaves / 2; m >= 1; m >>= 1) {
-      const double ob = __shfl_xor(bb, m, 64);
-      const int om = __shfl_xor(bm, m, 64);
+    for (int w = 1; w < kSchedWaves; ++w) {
+      const double ob = red_phi[w];
+      const int om = red_m[w];
       if (ob > bb || (ob == bb && om < bm)) {
         bb = ob;
         bm = om;
@@ -302,51 +335,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int B, int gamm
       lens[b] = cnt;
     }
   }
-}
-
-// Wave-wide scan and arg-max with DPP lane shifts (no LDS crossbar): row_shr
-// by 1, 2, 4 and 8 within each row of 16 lanes, then row_bcast:15 into rows
-// 1 and 3 and row_bcast:31 into rows 2 and 3.  Lanes whose source is outside
-// the row, or whose row is masked, receive the identity passed as `old`.
-template <int CTRL, int ROWM>
-__device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t x) {
-  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(x), CTRL, ROWM, 0xF, false));
-}
-template <int CTRL, int ROWM>
-__device__ __forceinline__ long long dpp_i64(long long v) {
-  const uint64_t u = uint64_t(v);
-  return (long long)((uint64_t(dpp32<CTRL, ROWM>(0u, uint32_t(u >> 32))) << 32) | dpp32<CTRL, ROWM>(0u, uint32_t(u)));
-}
-// inclusive prefix sum over the lanes of the wave
-__device__ __forceinline__ long long wave_scan_i64(long long v) {
-  v += dpp_i64<0x111, 0xF>(v);
-  v += dpp_i64<0x112, 0xF>(v);
-  v += dpp_i64<0x114, 0xF>(v);
-  v += dpp_i64<0x118, 0xF>(v);
-  v += dpp_i64<0x142, 0xA>(v);
-  v += dpp_i64<0x143, 0xC>(v);
-  return v;
-}
-template <int CTRL, int ROWM>
-__device__ __forceinline__ void dpp_argmax_step(double& b, int& m) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, b);
-  const uint32_t lo = dpp32<CTRL, ROWM>(0u, uint32_t(u));
-  const uint32_t hi = dpp32<CTRL, ROWM>(0xFFF00000u, uint32_t(u >> 32));   // -inf where no source
-  const int om = int(dpp32<CTRL, ROWM>(0x7FFFFFFFu, uint32_t(m)));
-  const double ob = __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
-  if (ob > b || (ob == b && om < m)) {
-    b = ob;
-    m = om;
-  }
-}
-// larger value, then smaller index, over the wave; the result is in lane 63
-__device__ __forceinline__ void wave_argmax_to_lane63(double& b, int& m) {
-  dpp_argmax_step<0x111, 0xF>(b, m);
-  dpp_argmax_step<0x112, 0xF>(b, m);
-  dpp_argmax_step<0x114, 0xF>(b, m);
-  dpp_argmax_step<0x118, 0xF>(b, m);
-  dpp_argmax_step<0x142, 0xA>(b, m);
-  dpp_argmax_step<0x143, 0xC>(b, m);
 }
 
 // Multi-workgroup scheduler.  No sort: the rank of a key is the number of
