@@ -115,10 +115,14 @@ size_t dspark_rnn_draft_workspace_bytes(int B, int gamma, int V, int r);
  *   conf    fp32  [B][gamma] out     c_k
  *   surv    fp32  [B][gamma] out     S_k
  *   workspace     >= dspark_draft_workspace_bytes(B, gamma, V, r) bytes,
- *                 256-byte aligned, zero-filled before its first use (e.g.
- *                 hipMemsetAsync).  Every call leaves it zero-filled again,
- *                 so it can be reused without clearing.  A workspace found
- *                 dirty is cleaned by the call, whose tokens are then all -1.
+ *                 256-byte aligned, zero-filled (e.g. hipMemsetAsync) before
+ *                 its first use and before any call whose B or gamma differs
+ *                 from the previous call's on it: its counters and arg-max
+ *                 slots sit at offsets that depend on B and gamma.  A call
+ *                 leaves them zero again, so calls of the same B and gamma
+ *                 reuse it without clearing.  A workspace found dirty by the
+ *                 barrier check is cleaned by the call, whose tokens are then
+ *                 all -1 (stale arg-max slots are not detected).
  * The call is one kernel launch.  If the kernel cannot synchronise its
  * workgroups (it never can deadlock: its waits are bounded) every token of
  * the call is -1.
@@ -144,8 +148,10 @@ dspark_status dspark_markov_draft(
  * memory comes from a static device array of DSPARK_NOALLOC_SCRATCH_BYTES
  * per GPU, held by the library until the process ends.  Its device address
  * is looked up on the first call on each device (that call also zero-fills
- * it with a small kernel on `stream`); every completed call leaves it
- * zero-filled again.  Nothing is allocated on any call.
+ * it with a small kernel on `stream`); every completed call leaves its
+ * counters and slots zero again, and a call whose B or gamma differs from the
+ * previous call's on the device first clears the part it needs with the same
+ * small kernel.  Nothing is allocated on any call.
  *   - Shapes whose dspark_draft_workspace_bytes(B, gamma, V, r) exceeds
  *     DSPARK_NOALLOC_SCRATCH_BYTES return DSPARK_ERR_UNSUPPORTED before
  *     anything is enqueued (B = 256, gamma = 16 needs about 1.1 MiB).
@@ -195,9 +201,10 @@ dspark_status dspark_markov_draft_noalloc(
  *   m_out     int32 [1] out  M*
  *   objective fp64  [1] out  Phi(M*) / 2^32 (may be NULL)
  *   workspace  NULL, or >= dspark_schedule_workspace_bytes(B, gamma) bytes,
- *              256-byte aligned, zero-filled before its first use; every
- *              call leaves it zero-filled again.  Calls sharing a workspace
- *              must not overlap.
+ *              256-byte aligned, its first 2048 bytes (ticket counters) zero
+ *              before its first use; every call leaves them zero again,
+ *              whatever B and gamma (the rest is scratch).  Calls sharing a
+ *              workspace must not overlap.
  * With a workspace the call is one launch of about B*gamma/16 workgroups
  * that rank the entries by comparison (no sort) and hand the scan, the
  * divisions and the arg-max to the last workgroup to finish; without one, a
@@ -422,12 +429,55 @@ dspark_status dspark_schedule_threshold(
  *   lens, accepted, bonus      int32 [iters][B] out
  *   m_out                      int32 [iters] out       scheduled drafts per iteration
  *   workspace                  >= dspark_serve_workspace_bytes(B, gamma, V, r) bytes, 256-byte
- *                              aligned, zero-filled before its first use (left zero-filled):
- *                              the drafting workspace, then the scheduler's
+ *                              aligned: the drafting workspace, then the scheduler's (whose
+ *                              counters follow the drafting part), zero-filled as the
+ *                              drafting workspace (before the first use and on a change of B
+ *                              or gamma)
  * Every argument is checked before the first launch; a HIP error later
  * leaves the iterations before it enqueued.  Limits: those of
  * dspark_markov_draft, and B * gamma <= 16384 for the GLOBAL policies.
  */
+/*
+ * dspark_step — one step of the path in one call: dspark_markov_draft, then
+ * dspark_schedule on the drafted survivals (with its workspace), then
+ * dspark_verify of the drafts against the target's tokens.
+ *
+ * Defined by: the three operations it chains (see dspark_markov_draft,
+ * dspark_schedule and dspark_verify for the passages); [P-blog] §3 (draft,
+ * schedule by confidence, verify the scheduled prefix).
+ *
+ * Outputs are exactly those of the three calls made in order on the same
+ * stream: tokens, logit, conf, surv [B][gamma]; lens, accepted, bonus [B];
+ * m_out [1] (the objective is not returned).
+ *
+ * Arguments: those of dspark_markov_draft (Markov head), followed by target
+ * [B][gamma + 1] and the step-cost table (t_step, n_min, n_count) as in
+ * dspark_verify and dspark_schedule, then the outputs.
+ *   workspace  >= dspark_step_workspace_bytes(B, gamma, V, r) bytes, 256-byte
+ *              aligned: the drafting workspace, then the scheduler's, zero-filled
+ *              as dspark_serve's (before the first use and on a change of B or
+ *              gamma).
+ * For bf16 storage at r = 256 on the whole-tile path with B * gamma <= 1024,
+ * the three run in one launch: after the last draft position every workgroup
+ * ranks its share of the survivals, and the workgroup that finishes last runs
+ * the scheduler's remaining steps and the verify (this saves the two launch
+ * gaps that dominate small batches).  Otherwise the call makes the three
+ * launches.  Errors and limits: the union of the three calls'.
+ */
+dspark_status dspark_step(
+    int B, int gamma, int V, int r, int d, dspark_dtype dtype,
+    const int32_t* anchor, const void* U, const void* h, const void* W1, const void* W2,
+    const float* conf_w, float conf_b, const float* sts_T, dspark_sampling mode, uint64_t seed,
+    const int32_t* target, const double* t_step, int n_min, int n_count,
+    int32_t* tokens, float* logit, float* conf, float* surv,
+    int32_t* lens, int32_t* m_out, int32_t* accepted, int32_t* bonus,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace dspark_step needs (the same as dspark_serve's): the
+ * drafting workspace plus the scheduler's.  Returns 0 for B*gamma == 0.  Needs
+ * no GPU. */
+size_t dspark_step_workspace_bytes(int B, int gamma, int V, int r);
+
 /* Bytes of workspace dspark_serve needs: dspark_draft_workspace_bytes plus
  * dspark_schedule_workspace_bytes.  Returns 0 for B*gamma == 0.  Needs no
  * GPU. */

@@ -8,4 +8,4 @@ Importing the functions below fails loudly if the library is not built.
 """
 from .binding import (markov_draft, parallel_draft, schedule, schedule_threshold, serve, sts_fit,  # noqa: F401
                       verify, workspace_bytes, library_path, set_draft_launch, get_draft_launch, rnn_draft,
-                      rnn_workspace_bytes, schedule_workspace_bytes)
+                      rnn_workspace_bytes, schedule_workspace_bytes, step)

@@ -61,6 +61,11 @@ def _declare(lib):
     lib.dspark_schedule_workspace_bytes.restype = c_size
     lib.dspark_serve_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
     lib.dspark_serve_workspace_bytes.restype = c_size
+    lib.dspark_step_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int]
+    lib.dspark_step_workspace_bytes.restype = c_size
+    lib.dspark_step.argtypes = ([c_int] * 6 + [c_vp] * 6 + [c_f, c_vp, c_int, c_u64] + [c_vp, c_vp, c_int, c_int] +
+                                [c_vp] * 8 + [c_vp, c_size, c_vp])
+    lib.dspark_step.restype = c_int
     lib.dspark_parallel_draft.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_int, c_u64, c_vp, c_vp, c_vp]
     lib.dspark_parallel_draft.restype = c_int
     lib.dspark_set_draft_launch.argtypes = [c_int]
@@ -154,21 +159,27 @@ def _workspace_key(kind: str, device_index: int, stream_handle: int):
     return (kind, int(device_index), int(stream_handle))
 
 
-def _workspace(nbytes: int, device, kind: str = "draft"):
+def _workspace(nbytes: int, device, kind: str = "draft", layout=None):
     """The cached workspace for the current stream of `device`, at least
     `nbytes` long.  A new one is zero-filled on that same stream, so the fill
-    is ordered before the call that uses it; every completed call leaves it
-    zero-filled again."""
+    is ordered before the call that uses it.  A call leaves the parts that
+    must start at zero (counters, arg-max slots) zero again, but where they
+    sit depends on the shape: when `layout` (the shape that fixes them)
+    differs from the previous call's, the reused buffer is zero-filled again
+    on the stream first."""
     torch = _torch()
     index = device.index if device.index is not None else torch.cuda.current_device()
     stream = torch.cuda.current_stream(index)
     key = _workspace_key(kind, index, stream.cuda_stream)
     with _lock:
-        ws = _ws_cache.get(key)
+        ws, last = _ws_cache.get(key, (None, None))
         if ws is None or ws.numel() < nbytes:
             with torch.cuda.stream(stream):
                 ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-            _ws_cache[key] = ws
+        elif layout != last:
+            with torch.cuda.stream(stream):
+                ws.zero_()
+        _ws_cache[key] = (ws, layout)
     return ws
 
 
@@ -207,7 +218,7 @@ def markov_draft(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, mode: str =
                torch.empty((B, gamma), dtype=torch.float32, device=dev))
     tokens, logit, conf, surv = out
     nbytes = workspace_bytes(B, gamma, V, r)
-    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev, "draft", (B, gamma))
     st = lib.dspark_markov_draft(
         B, gamma, V, r, d, DSPARK_BF16 if dt == torch.bfloat16 else DSPARK_F32,
         _ptr(anchor), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2),
@@ -217,6 +228,50 @@ def markov_draft(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, mode: str =
         _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
     _check(st)
     return tokens, logit, conf, surv
+
+
+def step(anchor, U, h, W1, W2, conf_w, conf_b: float, sts_T, target, t_step, n_min: int, mode: str = "greedy",
+         seed: int = 0, out=None, workspace=None):
+    """One step in one call (dspark_step): Markov-head drafting, the prefix
+    scheduler on the drafted survivals, and verify against `target` (int32
+    [B, gamma + 1]).  Returns (tokens, logit, conf, surv [B, gamma]; lens,
+    accepted, bonus [B]; m [1]).  Inputs as markov_draft; t_step fp64 and
+    n_min as schedule.  Without `workspace`, a library-owned workspace
+    cached per (device, stream) is used."""
+    torch = _torch()
+    lib = load()
+    _need(U, "U")
+    B, gamma, V = U.shape
+    dev = U.device
+    dt = U.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("U must be float32 or bfloat16")
+    r = W1.shape[1]
+    d = h.shape[2]
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(h, "h", dt, (B, gamma, d), dev)
+    _need(W1, "W1", dt, (V, r), dev)
+    _need(W2, "W2", dt, (r, V), dev)
+    _need(conf_w, "conf_w", torch.float32, (d + r,), dev)
+    _need(sts_T, "sts_T", torch.float32, (gamma,), dev)
+    _need(target, "target", torch.int32, (B, gamma + 1), dev)
+    _need(t_step, "t_step", torch.float64, None, dev)
+    if out is None:
+        f = lambda *sh, dtype=torch.float32: torch.empty(sh, dtype=dtype, device=dev)  # noqa: E731
+        out = (f(B, gamma, dtype=torch.int32), f(B, gamma), f(B, gamma), f(B, gamma), f(B, dtype=torch.int32),
+               f(B, dtype=torch.int32), f(B, dtype=torch.int32), f(1, dtype=torch.int32))
+    tokens, logit, conf, surv, lens, accepted, bonus, m = out
+    nbytes = int(lib.dspark_step_workspace_bytes(B, gamma, V, r))
+    ws = workspace if workspace is not None else _workspace(nbytes, dev, "step", (B, gamma))
+    st = lib.dspark_step(
+        B, gamma, V, r, d, DSPARK_BF16 if dt == torch.bfloat16 else DSPARK_F32,
+        _ptr(anchor), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2), _ptr(conf_w), ctypes.c_float(conf_b), _ptr(sts_T),
+        DSPARK_GUMBEL if mode == "gumbel" else DSPARK_GREEDY, ctypes.c_uint64(seed & (2 ** 64 - 1)),
+        _ptr(target), _ptr(t_step), int(n_min), int(t_step.numel()),
+        _ptr(tokens), _ptr(logit), _ptr(conf), _ptr(surv), _ptr(lens), _ptr(m), _ptr(accepted), _ptr(bonus),
+        _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    _check(st)
+    return tokens, logit, conf, surv, lens, accepted, bonus, m
 
 
 NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -290,7 +345,7 @@ def rnn_draft(anchor, U, h, W1, W2, decay, conf_w, conf_b: float, sts_T, mode: s
                torch.empty((B, gamma), dtype=torch.float32, device=dev))
     tokens, logit, conf, surv = out
     nbytes = rnn_workspace_bytes(B, gamma, V, r)
-    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev, "draft", (B, gamma))
     st = lib.dspark_rnn_draft(
         B, gamma, V, r, d, DSPARK_BF16,
         _ptr(anchor), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2), _ptr(decay),
@@ -429,7 +484,7 @@ def serve(anchor0, U, h, W1, W2, conf_w, conf_b: float, sts_T, target, t_step, n
                    accepted=f(iters, B, dtype=torch.int32), bonus=f(iters, B, dtype=torch.int32),
                    m=f(iters, dtype=torch.int32))
     nbytes = int(lib.dspark_serve_workspace_bytes(B, gamma, V, r))
-    ws = workspace if workspace is not None else _workspace(nbytes, dev, "serve")
+    ws = workspace if workspace is not None else _workspace(nbytes, dev, "serve", (B, gamma))
     st = lib.dspark_serve(
         iters, B, gamma, V, r, d, DSPARK_BF16 if dt == torch.bfloat16 else DSPARK_F32,
         _ptr(anchor0), _ptr(U), _ptr(h), _ptr(W1), _ptr(W2), _ptr(conf_w), ctypes.c_float(conf_b), _ptr(sts_T),

@@ -85,7 +85,8 @@ dspark_status draft_impl(int B, int gamma, int V, int r, int d, dspark_dtype dty
                          const void* U, const void* h, const void* W1, const void* W2, const float* decay,
                          bool rnn, const float* conf_w, float conf_b, const float* sts_T, dspark_sampling mode,
                          uint64_t seed, int32_t* tokens, float* logit, float* conf, float* surv, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream, bool noalloc = false) {
+                         size_t workspace_bytes, hipStream_t stream, bool noalloc = false,
+                         const dspark::StepArgs* step = nullptr, bool* fused = nullptr) {
   g_last_error[0] = '\0';
   if (B < 0 || gamma < 0 || V < 0 || r < 0 || d < 0)
     return fail(DSPARK_ERR_INVALID_ARG, "negative size");
@@ -143,8 +144,9 @@ dspark_status draft_impl(int B, int gamma, int V, int r, int d, dspark_dtype dty
   a.exclusive = g_draft_launch.load() == DSPARK_LAUNCH_EXCLUSIVE;
   a.decay = rnn ? decay : nullptr;
   a.noalloc = noalloc;
+  a.step = step;
   const char* why = nullptr;
-  hipError_t e = dspark::launch_markov_draft(a, stream, &why);
+  hipError_t e = dspark::launch_markov_draft(a, stream, &why, fused);
   if (why) return fail(DSPARK_ERR_UNSUPPORTED, "%s", why);
   if (e != hipSuccess) return hip_fail(e);
   return DSPARK_OK;
@@ -357,6 +359,57 @@ dspark_status dspark_verify(int B, int gamma, const int32_t* tokens, const int32
   if (!target || !lens || !accepted || !bonus || (gamma > 0 && !tokens))
     return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
   hipError_t e = dspark::launch_verify(B, gamma, tokens, target, lens, accepted, bonus, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return DSPARK_OK;
+}
+
+size_t dspark_step_workspace_bytes(int B, int gamma, int V, int r) { return dspark_serve_workspace_bytes(B, gamma, V, r); }
+
+dspark_status dspark_step(int B, int gamma, int V, int r, int d, dspark_dtype dtype, const int32_t* anchor,
+                          const void* U, const void* h, const void* W1, const void* W2, const float* conf_w,
+                          float conf_b, const float* sts_T, dspark_sampling mode, uint64_t seed,
+                          const int32_t* target, const double* t_step, int n_min, int n_count, int32_t* tokens,
+                          float* logit, float* conf, float* surv, int32_t* lens, int32_t* m_out, int32_t* accepted,
+                          int32_t* bonus, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || gamma < 0 || V < 0 || r < 0 || d < 0 || n_count < 1)
+    return fail(DSPARK_ERR_INVALID_ARG, "negative size or empty step-cost table");
+  if (B == 0) return DSPARK_OK;
+  if (!target || !t_step || !lens || !m_out || !accepted || !bonus)
+    return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+  if (n_min > B || (long long)n_min + n_count - 1 < B)
+    return fail(DSPARK_ERR_INVALID_ARG, "step-cost table must cover n = B (n_min <= B <= n_min + n_count - 1)");
+  if ((long long)B * gamma > dspark::kMaxScheduleItems) return fail(DSPARK_ERR_UNSUPPORTED, "B * gamma > 16384");
+  // the drafting workspace first, the scheduler's after it
+  const size_t draft_bytes = dspark_draft_workspace_bytes(B, gamma, V, r);
+  const size_t sched_bytes = dspark::schedule_workspace_bytes(B, gamma);
+  if (workspace && workspace_bytes >= draft_bytes && workspace_bytes - draft_bytes < sched_bytes)
+    return fail(DSPARK_ERR_WORKSPACE, "workspace smaller than dspark_step_workspace_bytes(B, gamma, V, r)");
+  if (gamma == 0) {   // nothing to draft or schedule: every length 0, bonus = target[b][0]
+    hipError_t e = dspark::launch_schedule(B, 0, nullptr, t_step, n_min, n_count, lens, m_out, nullptr, nullptr,
+                                           stream);
+    if (e == hipSuccess) e = dspark::launch_verify(B, 0, nullptr, target, lens, accepted, bonus, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return DSPARK_OK;
+  }
+  dspark::StepArgs st;
+  st.t_step = t_step;
+  st.n_min = n_min;
+  st.n_count = n_count;
+  st.target = target;
+  st.lens = lens;
+  st.m_out = m_out;
+  st.accepted = accepted;
+  st.bonus = bonus;
+  st.sched_ws = workspace ? static_cast<unsigned char*>(workspace) + draft_bytes : nullptr;
+  bool fused = false;
+  dspark_status ds = draft_impl(B, gamma, V, r, d, dtype, anchor, U, h, W1, W2, nullptr, false, conf_w, conf_b,
+                                sts_T, mode, seed, tokens, logit, conf, surv, workspace, workspace_bytes, stream,
+                                false, &st, &fused);
+  if (ds != DSPARK_OK || fused) return ds;
+  hipError_t e = dspark::launch_schedule(B, gamma, surv, t_step, n_min, n_count, lens, m_out, nullptr, st.sched_ws,
+                                         stream);
+  if (e == hipSuccess) e = dspark::launch_verify(B, gamma, tokens, target, lens, accepted, bonus, stream);
   if (e != hipSuccess) return hip_fail(e);
   return DSPARK_OK;
 }

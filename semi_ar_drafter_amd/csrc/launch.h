@@ -18,6 +18,18 @@ constexpr int kMaxGroupRows = 128;
 constexpr int kBarStride = 32;
 // Scheduler: one workgroup sorts all (request, position) keys in LDS.
 constexpr int kMaxScheduleItems = 16384;
+// dspark_step runs draft, schedule and verify in one launch up to this many
+// verify candidates (B * gamma), and makes three launches above it.
+constexpr int kFusedStepItems = 1024;
+
+// The schedule and verify part of a fused step (dspark_step).
+struct StepArgs {
+  const double* t_step;
+  int n_min, n_count;
+  const int32_t* target;
+  int32_t *lens, *m_out, *accepted, *bonus;
+  void* sched_ws;   // the scheduler's workspace (schedule_workspace_bytes)
+};
 
 struct DraftArgs {
   int B, gamma, V, r, d;
@@ -35,6 +47,7 @@ struct DraftArgs {
   bool exclusive;   // plain launch: the caller guarantees nothing else runs on the device
   const float* decay = nullptr;   // non-null: RNN head with this per-channel state decay [r] (bf16 only)
   bool noalloc = false;           // ws ignored: the per-device static scratch is used (Markov head)
+  const StepArgs* step = nullptr;  // non-null: schedule and verify in the same launch when the shape allows
 };
 
 // Workspace carve-up of the draft call (byte offsets, 256-aligned).
@@ -46,13 +59,18 @@ DraftWorkspace draft_workspace_layout(int B, int gamma, int r_state);
 
 // Returns hipSuccess or the first HIP error; sets *unsupported (with a reason)
 // when the shape is outside what the kernels handle.
-hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported);
+// *fused (optional) tells whether the schedule and verify of a.step ran in the
+// same launch (else the caller launches them).
+hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported,
+                               bool* fused = nullptr);
 
 // Allocation-free draft entry point: size of the per-device static scratch
 // that replaces the caller's workspace, and its device address (set up and
 // zero-filled on `stream` at the first call on the current device).
 constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
-hipError_t noalloc_scratch(hipStream_t stream, void** out);
+// A call whose shape (B << 32 | gamma) differs from the previous one on the
+// device clears the first zero_bytes (its counters and slots) first.
+hipError_t noalloc_scratch(hipStream_t stream, void** out, uint64_t shape, size_t zero_bytes);
 
 // Bytes of the multi-workgroup scheduler's workspace (0 for B*gamma == 0 or
 // above kMaxScheduleItems).

@@ -33,6 +33,7 @@
 //    clears the slots and counters for the next call, so a call is a single
 //    launch.
 #include "device_util.h"
+#include "rank_schedule.h"
 #include "launch.h"
 
 #include <mutex>
@@ -66,6 +67,13 @@ struct DraftParams {
   double* hdot;        // [B][gamma] hidden-state part of the confidence logit
   const float* decay;  // RNN head: per-channel decay of the recurrent state [r]
   uint16_t* state;     // RNN head: recurrent state, bf16 [2][B][r] (by step parity)
+  // fused step (the STEP kernels): the ranking scheduler and verify after the last draft position
+  unsigned int* sched_tickets;
+  RankEntry* sched_sorted;
+  const double* t_step;
+  int n_min, n_count, sched_e;
+  const int32_t* target;
+  int32_t *lens, *m_out, *accepted, *bonus;
 };
 
 // RNN head state step for four channels (a reading of the RNN head, whose
@@ -646,8 +654,61 @@ __device__ __forceinline__ double hidden_dot(const float* row, const float* w, i
 // FULL (bf16 only): V % 16 == 0, so every vocabulary tile is whole and rows
 // are 32-byte aligned, and every wave owns either no tile or at least two,
 // so the branch-free pair layout applies; otherwise the guarded path.
-template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL, bool RNN>
+// Fused step tail: the ranking scheduler (rank_phase / rank_tail) over the
+// survivals this launch has just written, on workgroups 0 .. G-1, then
+// verify of every request in the workgroup that ran the scheduler's tail.
+// `lds` is the U staging ring, idle once the last draft position is done.
+static_assert(kFusedStepItems <= 2 * kRankThreads, "the fused step ranks at most two keys per thread");
+
+template <int E, int K>
+__device__ __forceinline__ void step_tail(const DraftParams& p, int wg, uint32_t* lds) {
+  static_assert(K * kRankWaves <= 512, "counts fit the first 512 words");
+  const int n = p.B * p.gamma;
+  const int G = (n + K - 1) / K;
+  const RankShared<K> sh{reinterpret_cast<int(*)[kRankWaves]>(lds), reinterpret_cast<long long*>(lds + 512),
+                         reinterpret_cast<double*>(lds + 528), reinterpret_cast<int*>(lds + 544),
+                         reinterpret_cast<int*>(lds + 552), lds + 576};
+  if (wg >= G) return;
+  if (!rank_phase<E, K, true>(wg, G, p.B, p.gamma, p.surv, p.t_step, p.n_min, p.n_count, p.sched_tickets,
+                              p.sched_sorted, sh))
+    return;
+  rank_tail<E, K>(p.B, p.gamma, p.t_step, p.n_min, p.n_count, p.sched_tickets, p.sched_sorted, p.lens, p.m_out,
+                  nullptr, sh);
+  // verify: the longest prefix of the first lens[b] drafts that agrees with
+  // the target, and the target's token after it; a request's loads are
+  // issued eight positions at a time
+  const int gamma = p.gamma;
+  for (int b = threadIdx.x; b < p.B; b += kRankThreads) {
+    const int L = min(rank_count(sh.counters, b, gamma), gamma);
+    const int32_t* tk = p.tokens + size_t(b) * gamma;
+    const int32_t* tg = p.target + size_t(b) * (gamma + 1);
+    int a = 0;
+    bool go = true;
+    for (int k0 = 0; k0 < L && go; k0 += 8) {
+      int32_t x[8], y[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int kk = min(k0 + u, gamma - 1);
+        x[u] = load_dev(&tk[kk]);
+        y[u] = tg[kk];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (go && k0 + u < L) {
+          if (x[u] == y[u])
+            ++a;
+          else
+            go = false;
+        }
+    }
+    p.accepted[b] = a;
+    p.bonus[b] = tg[a];
+  }
+}
+
+template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL, bool RNN, bool STEP = false>
 __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p) {
+  static_assert(!STEP || (FULL && !RNN && NW * 64 == kRankThreads), "the fused step runs on the whole-tile kernel");
   static_assert(!RNN || BF16, "the RNN head is built for bf16 storage");
   typedef Elem<BF16> E;
   typedef typename E::store_t st_t;
@@ -906,7 +967,10 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     const int owner = part_of(int(x >> 4), p.tiles, nwg);
     const float z = __hip_atomic_load(&p.zpart[(size_t((kk & 1) * nwg + owner)) * B + b],
                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    p.tokens[size_t(b) * gamma + kk - 1] = int32_t(x);
+    if constexpr (STEP)   // read by the fused verify of another workgroup
+      store_dev(&p.tokens[size_t(b) * gamma + kk - 1], int32_t(x));
+    else
+      p.tokens[size_t(b) * gamma + kk - 1] = int32_t(x);
     p.logit[size_t(b) * gamma + kk - 1] = z;
     return int(x);
   };
@@ -1141,7 +1205,10 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
             const float S = lds_S[j] * cf;
             lds_S[j] = S;
             p.conf[size_t(b) * gamma + k - 1] = cf;
-            p.surv[size_t(b) * gamma + k - 1] = S;
+            if constexpr (STEP)   // ranked by every workgroup of the fused step
+              store_dev(&p.surv[size_t(b) * gamma + k - 1], S);
+            else
+              p.surv[size_t(b) * gamma + k - 1] = S;
           }
         }
       }
@@ -1184,7 +1251,20 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     const uint64_t key = load_dev(&p.slots[size_t(gamma - 1) * B + b]);
     emit(b, gamma, key);
     if (failed)
-      for (int kk = 0; kk < gamma; ++kk) p.tokens[size_t(b) * gamma + kk] = -1;
+      for (int kk = 0; kk < gamma; ++kk) {
+        if constexpr (STEP)
+          store_dev(&p.tokens[size_t(b) * gamma + kk], -1);
+        else
+          p.tokens[size_t(b) * gamma + kk] = -1;
+      }
+  }
+
+  if constexpr (STEP) {
+    __syncthreads();   // the staging ring is idle from here on
+    if (p.sched_e == 1)
+      step_tail<1, 16>(p, wg, lds_u);
+    else
+      step_tail<2, 16>(p, wg, lds_u);
   }
 
   // Leave the workspace as a fresh call expects it: once every workgroup is
@@ -1217,9 +1297,19 @@ struct KernelChoice {
 constexpr int kDraftWaves = 8;
 
 template <bool BF16, int R, bool G, bool RNN>
-KernelChoice pick_r(bool full, int tiles_per_wave) {
+KernelChoice pick_r(bool full, int tiles_per_wave, bool step) {
   constexpr int NW = kDraftWaves, GR = kMaxGroupRows;
   constexpr int TPW = BF16 ? 5 : 4;
+  if constexpr (BF16 && R == 256 && !RNN) {
+    // the fused draft-schedule-verify step (whole tiles only)
+    if (step && full) {
+      if (tiles_per_wave <= 4)
+        return KernelChoice{
+            reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, 4, GR, G, true, RNN, true>), NW * 64, 4};
+      return KernelChoice{
+          reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, true, RNN, true>), NW * 64, TPW};
+    }
+  }
   if constexpr (BF16) {
     // rank 256, Markov head: four tiles per wave when they cover the
     // vocabulary (W2 then takes 128 instead of 160 registers per lane and no
@@ -1237,22 +1327,22 @@ KernelChoice pick_r(bool full, int tiles_per_wave) {
 }
 
 template <bool G>
-bool pick(bool bf16, int r, bool full, bool rnn, int tpw_need, KernelChoice* out) {
+bool pick(bool bf16, int r, bool full, bool rnn, int tpw_need, KernelChoice* out, bool step = false) {
   const int n = tpw_need;
   if (bf16) {
     switch (r) {
-      case 32: *out = rnn ? pick_r<true, 32, G, true>(full, n) : pick_r<true, 32, G, false>(full, n); return true;
-      case 64: *out = rnn ? pick_r<true, 64, G, true>(full, n) : pick_r<true, 64, G, false>(full, n); return true;
-      case 128: *out = rnn ? pick_r<true, 128, G, true>(full, n) : pick_r<true, 128, G, false>(full, n); return true;
-      case 256: *out = rnn ? pick_r<true, 256, G, true>(full, n) : pick_r<true, 256, G, false>(full, n); return true;
+      case 32: *out = rnn ? pick_r<true, 32, G, true>(full, n, false) : pick_r<true, 32, G, false>(full, n, false); return true;
+      case 64: *out = rnn ? pick_r<true, 64, G, true>(full, n, false) : pick_r<true, 64, G, false>(full, n, false); return true;
+      case 128: *out = rnn ? pick_r<true, 128, G, true>(full, n, false) : pick_r<true, 128, G, false>(full, n, false); return true;
+      case 256: *out = rnn ? pick_r<true, 256, G, true>(full, n, false) : pick_r<true, 256, G, false>(full, n, step); return true;
       default: return false;
     }
   }
   if (rnn) return false;
   switch (r) {
-    case 16: *out = pick_r<false, 16, G, false>(full, n); return true;
-    case 32: *out = pick_r<false, 32, G, false>(full, n); return true;
-    case 64: *out = pick_r<false, 64, G, false>(full, n); return true;
+    case 16: *out = pick_r<false, 16, G, false>(full, n, false); return true;
+    case 32: *out = pick_r<false, 32, G, false>(full, n, false); return true;
+    case 64: *out = pick_r<false, 64, G, false>(full, n, false); return true;
     default: return false;
   }
 }
@@ -1314,8 +1404,9 @@ DraftWorkspace draft_workspace_layout(int B, int gamma, int r_state) {
   return w;
 }
 
-hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported) {
+hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const char** unsupported, bool* fused) {
   *unsupported = nullptr;
+  if (fused) *fused = false;
   KernelChoice kc;
   const bool rnn = a.decay != nullptr;
   if (!(a.gumbel ? pick<true>(a.bf16, a.r, false, rnn, 0, &kc) : pick<false>(a.bf16, a.r, false, rnn, 0, &kc))) {
@@ -1334,12 +1425,22 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   // the pair layout needs at least two tiles in every wave's range
   const bool full = (a.V % 16) == 0 && (tiles / nwg) / kDraftWaves >= 2;
   const int per_wg = (tiles + nwg - 1) / nwg;
+  // The fused step, for at most kFusedStepItems verify candidates (one or
+  // two ranking keys per thread, 16 keys per ranking workgroup): the ranking
+  // workgroups must fit in the draft grid, and the last one's verify follows.
+  // Larger batches take three launches: their drafting kernel is bandwidth
+  // bound, and the fused kernel's extra registers slow its tile loop by about
+  // as much as the two launches it saves.
+  const long long n_items = (long long)a.B * a.gamma;
+  const int sched_e = n_items <= kRankThreads ? 1 : 2;
+  const bool step = a.step != nullptr && full && a.bf16 && a.r == 256 && !rnn && !a.noalloc &&
+                    n_items <= kFusedStepItems && (n_items + 15) / 16 <= nwg;
   if (full) {
     const int tpw_need = (per_wg + kDraftWaves - 1) / kDraftWaves;   // most tiles any wave owns
     if (a.gumbel)
-      pick<true>(a.bf16, a.r, true, rnn, tpw_need, &kc);
+      pick<true>(a.bf16, a.r, true, rnn, tpw_need, &kc, step);
     else
-      pick<false>(a.bf16, a.r, true, rnn, tpw_need, &kc);
+      pick<false>(a.bf16, a.r, true, rnn, tpw_need, &kc, step);
   }
   const int nwaves = kc.threads / 64;
   if ((per_wg + nwaves - 1) / nwaves > kc.tpw) {
@@ -1358,7 +1459,9 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
       return hipSuccess;
     }
     void* sp = nullptr;
-    e = noalloc_scratch(stream, &sp);
+    // the counters and arg-max slots of this shape: [0, end of the slots)
+    const size_t zero_bytes = L.slots + size_t(a.gamma) * a.B * sizeof(uint64_t);
+    e = noalloc_scratch(stream, &sp, (uint64_t(uint32_t(a.B)) << 32) | uint32_t(a.gamma), zero_bytes);
     if (e != hipSuccess) return e;
     ws = static_cast<char*>(sp);
   }
@@ -1397,6 +1500,27 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   p.hdot = reinterpret_cast<double*>(ws + L.hdot);
   p.decay = a.decay;
   p.state = rnn ? reinterpret_cast<uint16_t*>(ws + L.state) : nullptr;
+  p.sched_tickets = nullptr;
+  p.sched_sorted = nullptr;
+  p.t_step = nullptr;
+  p.n_min = p.n_count = p.sched_e = 0;
+  p.target = nullptr;
+  p.lens = p.m_out = p.accepted = p.bonus = nullptr;
+  if (step) {
+    unsigned char* sws = static_cast<unsigned char*>(a.step->sched_ws);
+    p.sched_tickets = reinterpret_cast<unsigned int*>(sws);
+    p.sched_sorted = reinterpret_cast<RankEntry*>(sws + kRankHeader);
+    p.t_step = a.step->t_step;
+    p.n_min = a.step->n_min;
+    p.n_count = a.step->n_count;
+    p.sched_e = sched_e;
+    p.target = a.step->target;
+    p.lens = a.step->lens;
+    p.m_out = a.step->m_out;
+    p.accepted = a.step->accepted;
+    p.bonus = a.step->bonus;
+    if (fused) *fused = true;
+  }
 
   // Every workgroup must be resident at once (grid barriers between draft
   // positions; nwg <= one per compute unit).  The cooperative launch
@@ -1411,11 +1535,14 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
 // Address of this device's scratch, set up on the first call per device:
 // hipGetSymbolAddress with the device current, then one zero-fill on
 // `stream` (ordered before the draft launch that follows on the same stream).
-// Later calls find the scratch zero-filled by the previous call's last phase.
-hipError_t noalloc_scratch(hipStream_t stream, void** out) {
+// A later call of the same shape finds its counters and slots zero (left so
+// by the previous call's last phase); a call of another shape (B, gamma) has
+// them elsewhere, so the first `zero_bytes` are cleared again first.
+hipError_t noalloc_scratch(hipStream_t stream, void** out, uint64_t shape, size_t zero_bytes) {
   constexpr int kMaxDevices = 64;
   static std::mutex mu;
   static void* addr[kMaxDevices] = {};
+  static uint64_t last_shape[kMaxDevices] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -1431,6 +1558,13 @@ hipError_t noalloc_scratch(hipStream_t stream, void** out) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     addr[dev] = p;
+    last_shape[dev] = shape;
+  } else if (shape != last_shape[dev]) {
+    const size_t n16 = (zero_bytes + 15) / 16;
+    scratch_clear_kernel<<<dim3(64), dim3(256), 0, stream>>>(static_cast<u32x4_t*>(addr[dev]), n16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    last_shape[dev] = shape;
   }
   *out = addr[dev];
   return hipSuccess;

@@ -252,6 +252,32 @@ def test_serve_validation(lib):
     assert lib.dspark_last_error().decode() != ""
 
 
+def test_step_validation(lib):
+    need = lib.dspark_step_workspace_bytes(4, 4, 1024, 32)
+    assert need == lib.dspark_serve_workspace_bytes(4, 4, 1024, 32) > lib.dspark_draft_workspace_bytes(4, 4, 1024, 32)
+
+    def step(B=4, g=4, V=1024, r=32, d=16, dt=1, n_min=4, n_count=17, ws=P, ws_bytes=None, mode=0, **over):
+        ptr = dict(anchor=P, U=P, h=P, W1=P, W2=P, conf_w=P, sts_T=P, target=P, t_step=P, tokens=P, logit=P,
+                   conf=P, surv=P, lens=P, m=P, accepted=P, bonus=P)
+        ptr.update(over)
+        return lib.dspark_step(B, g, V, r, d, dt, ptr["anchor"], ptr["U"], ptr["h"], ptr["W1"], ptr["W2"],
+                               ptr["conf_w"], ctypes.c_float(1.0), ptr["sts_T"], mode, 0, ptr["target"],
+                               ptr["t_step"], n_min, n_count, ptr["tokens"], ptr["logit"], ptr["conf"], ptr["surv"],
+                               ptr["lens"], ptr["m"], ptr["accepted"], ptr["bonus"], ws,
+                               ctypes.c_size_t(need if ws_bytes is None else ws_bytes), NULL)
+
+    assert step(B=-1) == INVALID and step(n_count=0) == INVALID
+    assert step(B=0) == OK                                   # no-op, nothing launched
+    for k in ("target", "t_step", "lens", "m", "accepted", "bonus"):
+        assert step(**{k: NULL}) == INVALID, k
+    assert step(n_min=5) == INVALID and step(n_min=0, n_count=4) == INVALID
+    assert step(B=4097, g=4, n_min=4097, n_count=16389, ws_bytes=1 << 40) == UNSUPPORTED   # B * gamma > 16384
+    assert step(ws_bytes=lib.dspark_draft_workspace_bytes(4, 4, 1024, 32)) == WORKSPACE   # no room for the scheduler
+    assert step(ws=NULL) == WORKSPACE
+    assert step(anchor=NULL) == INVALID and step(dt=5) == INVALID and step(mode=3) == INVALID
+    assert lib.dspark_last_error().decode() != ""
+
+
 def test_draft_launch_mode_setting(lib):
     assert lib.dspark_get_draft_launch() == 0                 # cooperative by default
     assert lib.dspark_set_draft_launch(1) == OK and lib.dspark_get_draft_launch() == 1
@@ -285,12 +311,19 @@ def test_workspace_cache_is_per_device_and_stream(monkeypatch):
 
     made = []
 
+    zeroed = []
+
     class Buf:
         def __init__(self, n, device, stream):
             self.n, self.device, self.stream = n, device, stream
 
         def numel(self):
             return self.n
+
+        def zero_(self):
+            assert Cuda.active is not None, "the re-fill must be enqueued on the caller's stream"
+            zeroed.append((self, Cuda.active.cuda_stream))
+            return self
 
     class Cuda:
         current = {0: Stream(0x100), 1: Stream(0x200)}
@@ -344,3 +377,8 @@ def test_workspace_cache_is_per_device_and_stream(monkeypatch):
     assert s is not c
     assert len(made) == 5
     assert binding._workspace_key("draft", 0, 0x100) != binding._workspace_key("draft", 0, 0x300)
+    # the zero-required parts move with the shape: a change of layout re-fills the reused buffer
+    f = binding._workspace(100, d0, "step", (96, 6))
+    assert binding._workspace(100, d0, "step", (96, 6)) is f and not zeroed      # same shape: as left
+    assert binding._workspace(90, d0, "step", (40, 16)) is f and zeroed == [(f, 0x300)]
+    assert binding._workspace(90, d0, "step", (40, 16)) is f and len(zeroed) == 1

@@ -1,0 +1,125 @@
+"""dspark_step (draft, schedule and verify in one call) against the three
+calls it chains, made in order on the same inputs: every output bit for bit.
+Whole-tile bf16 rank-256 shapes with B*gamma <= 1024 run as one launch
+(after the last draft position the scheduler's ranking workgroups, then the
+verify, in the same kernel); the others as three launches.  The three calls themselves are
+compared with the oracle by the parity tests; here the oracle also re-derives
+the lengths from the returned survivals and the verify from the returned
+tokens."""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from oracle import dspark_oracle as orc  # noqa: E402
+from semi_ar_drafter_amd import binding  # noqa: E402
+from semi_ar_drafter_amd import workloads as wl  # noqa: E402
+
+from parity import to_device  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+    yield
+    binding.set_draft_launch("cooperative")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+NAMES = ("tokens", "logit", "conf", "surv", "lens", "accepted", "bonus", "m")
+
+
+def separate(d, ws_sched):
+    args = (d["anchor"], d["U"], d["h"], d["W1"], d["W2"], d["conf_w"], d["conf_b"], d["sts_T"])
+    tok, logit, conf, surv = binding.markov_draft(*args, mode=d["mode"], seed=d["seed"])
+    lens, m, _ = binding.schedule(surv, d["t_step"], d["n_min"], workspace=ws_sched)
+    acc, bonus = binding.verify(tok, d["target"], lens)
+    return tok, logit, conf, surv, lens, acc, bonus, m
+
+
+def fused(d, ws=None):
+    args = (d["anchor"], d["U"], d["h"], d["W1"], d["W2"], d["conf_w"], d["conf_b"], d["sts_T"])
+    return binding.step(*args, d["target"], d["t_step"], d["n_min"], mode=d["mode"], seed=d["seed"], workspace=ws)
+
+
+def compare(d, label, repeats=2):
+    B, g = d["U"].shape[0], d["U"].shape[1]
+    ws_sched = torch.zeros(max(binding.schedule_workspace_bytes(B, g), 256), dtype=torch.uint8, device="cuda:0")
+    ref = [x.cpu().numpy() for x in separate(d, ws_sched)]
+    for rep in range(repeats):     # the same workspace again: the call left it ready
+        got = [x.cpu().numpy() for x in fused(d)]
+        torch.cuda.synchronize()
+        for name, a, b in zip(NAMES, ref, got):
+            assert a.shape == b.shape, (label, name)
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (label, rep, name)
+    tok, surv, lens, acc, bonus, m = got[0], got[3], got[4], got[5], got[6], got[7]
+    o_lens, o_m, _ = orc.schedule(surv, d["t_step"].cpu().numpy(), d["n_min"])
+    assert int(m[0]) == o_m and (lens == o_lens).all(), label
+    o_acc, o_bonus = orc.verify(tok, d["target"].cpu().numpy(), lens)
+    assert (acc == o_acc).all() and (bonus == o_bonus).all(), label
+    assert ((tok >= 0) & (tok < d["U"].shape[2])).all(), label
+    return got
+
+
+CASES = {
+    "whole-tile greedy": dict(B=96, gamma=6, V=69632, r=256, d=48, dtype="bf16"),
+    "whole-tile gumbel": dict(B=40, gamma=16, V=65536, r=256, d=32, dtype="bf16", sampling="gumbel"),
+    "one request": dict(B=1, gamma=8, V=65536, r=256, d=32, dtype="bf16"),
+    "fused limit, two keys per thread": dict(B=64, gamma=16, V=65536, r=256, d=32, dtype="bf16"),
+    "five slots per wave, gumbel": dict(B=8, gamma=16, V=151936, r=256, d=32, dtype="bf16", sampling="gumbel"),
+    "above the fused limit": dict(B=65, gamma=16, V=65536, r=256, d=32, dtype="bf16"),
+    "three launches, bf16 r=32": dict(B=10, gamma=3, V=3001, r=32, d=20, dtype="bf16", sampling="gumbel"),
+    "three launches, fp32": dict(B=5, gamma=4, V=1030, r=16, d=12, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("launch", ["exclusive", "cooperative"])
+def test_step_equals_three_calls(name, launch):
+    shape = dict(CASES[name])
+    sampling = shape.pop("sampling", "greedy")
+    w = wl.make_workload(wl.small_config(sampling=sampling, **shape))
+    say(f"[case] step {name} {launch}")
+    binding.set_draft_launch(launch)
+    compare(to_device(w), name)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_step_full_size(cid):
+    """The full-size workloads: B*gamma = 8 and 1024 (one launch), 4096 and
+    8192 (three launches; the last with Gumbel-max sampling)."""
+    w = wl.make_workload(wl.WORKLOADS[cid])
+    say(f"[case] step full size config {cid}")
+    binding.set_draft_launch("exclusive")
+    compare(to_device(w), f"config {cid}", repeats=1)
+
+
+def test_step_largest_schedule():
+    """B*gamma = 16384, the scheduler's largest input (three launches),
+    random inputs made on the GPU."""
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    B, gamma, V, r, d = 256, 64, 65536, 256, 64
+    say(f"[case] step B={B} gamma={gamma} V={V}")
+    dev = "cuda:0"
+    dd = dict(anchor=torch.randint(0, V, (B,), generator=g, device=dev, dtype=torch.int32),
+              U=(torch.randn(B, gamma, V, generator=g, device=dev) * 2).bfloat16(),
+              h=torch.randn(B, gamma, d, generator=g, device=dev).bfloat16(),
+              W1=(torch.randn(V, r, generator=g, device=dev) * 0.25).bfloat16(),
+              W2=(torch.randn(r, V, generator=g, device=dev) * 0.25).bfloat16(),
+              conf_w=torch.randn(d + r, generator=g, device=dev) * 0.05, conf_b=0.3,
+              sts_T=torch.linspace(1.0, 1.5, gamma, device=dev),
+              target=torch.randint(0, V, (B, gamma + 1), generator=g, device=dev, dtype=torch.int32),
+              t_step=torch.from_numpy(4.0 + 0.02 * np.arange(B, B + B * gamma + 1, dtype=np.float64)).to(dev),
+              n_min=B, seed=5, mode="greedy")
+    binding.set_draft_launch("exclusive")
+    compare(dd, "largest schedule", repeats=1)
