@@ -85,9 +85,14 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
 // within 2^-24 of 1, where 1 - u is tiny; L = -ln u >= 5.9e-8 is a normal
 // number, so the outer logarithm is as accurate, and the absolute error of G
 // stays around 1e-6.
+//
+// u is formed in two instructions: one funnel shift puts the top 23 bits of
+// w under the exponent of 1.0 (the float 1 + (w >> 9) * 2^-23), and
+// subtracting 1 - 2^-24 leaves (2 (w >> 9) + 1) * 2^-24 exactly (the operands
+// are within a factor of two of each other, so the difference is exact).
 __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
-  const uint32_t m2 = (w >> 9) * 2u + 1u;
-  const float u = float(m2) * 0x1p-24f;
+  const float one_plus = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9u));
+  const float u = one_plus - 0x1.fffffep-1f;
   const float ln2 = 0.693147180559945309f;
   const float l = -__builtin_amdgcn_logf(u) * ln2;
   return -__builtin_amdgcn_logf(l) * ln2;
