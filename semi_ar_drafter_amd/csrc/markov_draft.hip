@@ -723,7 +723,13 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   constexpr int CMAX = TPW * NW * 16;                       // widest column slice of a workgroup
   constexpr int SLD = CMAX + (BF16 ? 8 : 4);                // W2 staging row stride (16-byte multiple)
   constexpr int EBUF = (GR * LDE > E::KS * SLD) ? GR * LDE : E::KS * SLD;
-  __shared__ __attribute__((aligned(16))) st_t lds_e[EBUF];
+  // the embedding buffer and the U staging ring share one array, the
+  // embeddings first: B-fragment reads then address them with the LDS
+  // instruction's immediate offset
+  constexpr int EWORDS = int((EBUF * sizeof(st_t) + 15) / 16) * 4;
+  constexpr int UWORDS = FULL ? NW * 3 * 768 : 4;
+  __shared__ __attribute__((aligned(16))) uint32_t lds_eu[EWORDS + UWORDS];
+  st_t* const lds_e = reinterpret_cast<st_t*>(lds_eu);
   __shared__ uint64_t lds_key[GR];
   __shared__ float lds_z[NW][GR];
   __shared__ int lds_x[GR];
@@ -733,7 +739,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   __shared__ float lds_dec[RNN ? R : 1];                // RNN head: decay
   __shared__ double lds_ce[RNN ? kMaxOwnedRows : 1];    // RNN head: embedding half of owned rows' confidence dots
   // U staging ring of the whole-tile path: three slots of 3 KB per wave
-  __shared__ __attribute__((aligned(16))) uint32_t lds_u[FULL ? NW * 3 * 768 : 4];
+  uint32_t* const lds_u = lds_eu + EWORDS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -770,7 +776,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   // coalesced row loads; each wave then picks its fragments out of LDS.
   frag_t A[TPW][NKS];
   if constexpr (!FULL) {
-    constexpr int KCH0 = int(sizeof(lds_e) / (SLD * sizeof(st_t)));
+    constexpr int KCH0 = int(EBUF / SLD);
     constexpr int KCH = (KCH0 >= R) ? R : (KCH0 / E::KS) * E::KS;   // K rows per chunk
     static_assert(KCH >= E::KS, "staging buffer too small");
     st_t* stage = lds_e;
@@ -846,7 +852,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     // 16-byte piece of a (b, k) row in flight at once.
     constexpr int EPC = 8;                                    // bf16 per 16-byte piece
     constexpr int PER = (E::KS * (CMAX / EPC) + NT - 1) / NT; // pieces per thread and chunk
-    static_assert(E::KS * SLD <= EBUF && E::KS * SLD * int(sizeof(st_t)) <= int(sizeof(lds_u)),
+    static_assert(E::KS * SLD <= EBUF && E::KS * SLD * int(sizeof(st_t)) <= UWORDS * int(sizeof(uint32_t)),
                   "W2 staging buffers");
     const st_t* W2 = static_cast<const st_t*>(p.W2);
     const int col0 = wg_lo * 16;
@@ -884,7 +890,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     const int hpc = p.d / 8;                                   // pieces per row
     // (d = 0, where h may be null and every dot is 0, takes the generic loop, which reads nothing)
     const bool fast_hd = p.d > 0 && (p.d % 8) == 0 && hpc <= 64 * HJ &&
-                         p.d <= int(sizeof(lds_u) / sizeof(float)) && (reinterpret_cast<uintptr_t>(h) & 15) == 0;
+                         p.d <= UWORDS && (reinterpret_cast<uintptr_t>(h) & 15) == 0;
     if (fast_hd) {
       float* wl = reinterpret_cast<float*>(lds_u);
       for (int i = tid; i < p.d; i += NT) wl[i] = p.conf_w[i];
