@@ -489,12 +489,24 @@ struct TileWork {
     if constexpr (GUMBEL) {
       // the winner's unperturbed logit travels with the key
       bz = (bi == 0) ? bzsel[0] : (bi == 1) ? bzsel[1] : (bi == 2) ? bzsel[2] : bzsel[3];
+      // the four lane groups' candidates of a request reduced by the gfx950
+      // row swaps: swapping a value with itself leaves rows 0 and 2 (16
+      // apart) or the lower half (32 apart) in one register and their
+      // partners in the other, so the larger of the two is the pair's best
+      // in every lane
 #pragma unroll
       for (int m = 16; m <= 32; m <<= 1) {
-        const uint64_t ok = shfl_xor_u64(key, m);
-        const float oz = __shfl_xor(bz, m, 64);
-        if (ok > key) bz = oz;
-        key = ok > key ? ok : key;
+        uint32_t kl = uint32_t(key), kh = uint32_t(key >> 32), zb = __float_as_uint(bz);
+        const auto sl = (m == 16) ? __builtin_amdgcn_permlane16_swap(kl, kl, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(kl, kl, false, false);
+        const auto sh = (m == 16) ? __builtin_amdgcn_permlane16_swap(kh, kh, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(kh, kh, false, false);
+        const auto sz = (m == 16) ? __builtin_amdgcn_permlane16_swap(zb, zb, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(zb, zb, false, false);
+        const uint64_t a = (uint64_t(sh[0]) << 32) | sl[0], b = (uint64_t(sh[1]) << 32) | sl[1];
+        const bool tb = b > a;
+        key = tb ? b : a;
+        bz = __uint_as_float(tb ? sz[1] : sz[0]);
       }
     }
     return key;
