@@ -457,8 +457,8 @@ dspark_status dspark_schedule_threshold(
  *              aligned: the drafting workspace, then the scheduler's, zero-filled
  *              as dspark_serve's (before the first use and on a change of B or
  *              gamma).
- * For bf16 storage at r = 256 on the whole-tile path with B * gamma <= 1024,
- * the three run in one launch: after the last draft position every workgroup
+ * For bf16 storage at r = 256 on the whole-tile path with 8 < B and
+ * B * gamma <= 1024, the three run in one launch: after the last draft position every workgroup
  * ranks its share of the survivals, and the workgroup that finishes last runs
  * the scheduler's remaining steps and the verify (this saves the two launch
  * gaps that dominate small batches).  Otherwise the call makes the three

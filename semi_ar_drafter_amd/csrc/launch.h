@@ -13,6 +13,9 @@ constexpr int kMaxDraftWorkgroups = 512;
 constexpr int kMaxOwnedRows = 64;
 // Requests per group in the draft kernel (LDS holds one group's embeddings).
 constexpr int kMaxGroupRows = 128;
+// Batches of at most this many requests synchronise the draft positions
+// through per-workgroup winner keys instead of arrival counters.
+constexpr int kSmallBatch = 8;
 // Distance (in 32-bit words) between the per-group arrival counters (one
 // 128-byte line each: every workgroup polls them).
 constexpr int kBarStride = 32;
@@ -50,9 +53,11 @@ struct DraftArgs {
   const StepArgs* step = nullptr;  // non-null: schedule and verify in the same launch when the shape allows
 };
 
-// Workspace carve-up of the draft call (byte offsets, 256-aligned).
+// Workspace carve-up of the draft call (byte offsets, 256-aligned).  Every
+// section before zpart must be zero when a call starts (each call leaves it
+// so); wkeys and wz are empty unless B <= kSmallBatch.
 struct DraftWorkspace {
-  size_t ctrl, bar, slots, zpart, hdot, state, total;
+  size_t ctrl, bar, slots, wkeys, wz, zpart, hdot, state, total;
 };
 // r_state: the RNN head's rank (its bf16 state [2][B][r] is carved out too), 0 for the Markov head.
 DraftWorkspace draft_workspace_layout(int B, int gamma, int r_state);

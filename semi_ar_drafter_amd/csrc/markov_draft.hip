@@ -67,6 +67,11 @@ struct DraftParams {
   double* hdot;        // [B][gamma] hidden-state part of the confidence logit
   const float* decay;  // RNN head: per-channel decay of the recurrent state [r]
   uint16_t* state;     // RNN head: recurrent state, bf16 [2][B][r] (by step parity)
+  // small batches (the SMALL kernels): every workgroup's winner key of (step k, request b) at
+  // wkeys[(k * B + b) * nwg + wg], written once per call (0 = not yet written), and for Gumbel
+  // sampling the winner's unperturbed logit as ~bits at the same index of wz
+  uint64_t* wkeys;
+  uint32_t* wz;
   // fused step (the STEP kernels): the ranking scheduler and verify after the last draft position
   unsigned int* sched_tickets;
   RankEntry* sched_sorted;
@@ -718,9 +723,73 @@ __device__ __forceinline__ void step_tail(const DraftParams& p, int wg, uint32_t
   }
 }
 
-template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL, bool RNN, bool STEP = false>
+// Small batches: the largest of the n keys row[0..n) (one per workgroup,
+// each written once per call with a device-scope store, never 0 once
+// written), read by a whole wave, which polls until every entry is there.
+// The spin is bounded like a grid barrier's: past `limit` polls the error
+// flag is raised, and a raised flag ends the wait.
+__device__ __forceinline__ uint64_t small_max(const uint64_t* row, int n, int lane, unsigned int* err,
+                                              unsigned int limit) {
+  constexpr int PER = kMaxDraftWorkgroups / 64;
+  uint32_t need = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lane + 64 * i < n) need |= 1u << i;
+  uint64_t best = 0ull;
+  unsigned int polls = 0;
+  for (;;) {
+    uint64_t v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = ((need >> i) & 1u) ? load_dev(row + lane + 64 * i) : 0ull;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (v[i] != 0ull) {
+        best = v[i] > best ? v[i] : best;
+        need &= ~(1u << i);
+      }
+    if (!__any(need != 0u)) break;
+    if (++polls > limit) {
+      if (lane == 0) store_dev(err, 1u);
+      break;
+    }
+    if ((polls & 15u) == 0u && load_dev(err) != 0u) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(best, m);
+    best = o > best ? o : best;
+  }
+  return best;
+}
+
+// Small batches, Gumbel sampling: the unperturbed logit a workgroup stored
+// (as ~bits, never 0) beside its winner key; one thread polls, bounded.
+__device__ __forceinline__ float small_logit(const uint32_t* at, unsigned int* err, unsigned int limit) {
+  uint32_t v = load_dev(at);
+  unsigned int polls = 0;
+  while (v == 0u) {
+    if (++polls > limit || load_dev(err) != 0u) {
+      store_dev(err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = load_dev(at);
+  }
+  return __uint_as_float(~v);
+}
+
+// SMALL (B <= kSmallBatch, one request group): instead of the per-step
+// arrival counter and the arg-max slots, every workgroup stores its winner
+// key of each request once (wkeys), and a reader waits for the keys
+// themselves: no atomic to complete before an arrival, no counter round
+// trip, no separate slot read.
+template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL, bool RNN, bool STEP = false,
+          bool SMALL = false>
 __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p) {
   static_assert(!STEP || (FULL && !RNN && NW * 64 == kRankThreads), "the fused step runs on the whole-tile kernel");
+  static_assert(!SMALL || (!RNN && !STEP && kSmallBatch <= NW && kSmallBatch <= 16),
+                "one wave per request of one group; no fused step");
   static_assert(!RNN || BF16, "the RNN head is built for bf16 storage");
   typedef Elem<BF16> E;
   typedef typename E::store_t st_t;
@@ -745,6 +814,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   __shared__ uint64_t lds_key[GR];
   __shared__ float lds_z[NW][GR];
   __shared__ int lds_x[GR];
+  __shared__ uint64_t lds_sk[SMALL ? NW : 1];   // SMALL: the previous step's key of each request
   __shared__ double lds_hd[GR];
   __shared__ float lds_S[kMaxOwnedRows];
   __shared__ float lds_we[R];   // confidence weights of the Markov-embedding half
@@ -983,8 +1053,14 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     uint32_t x = key_index(key);
     if (key == 0ull || x >= uint32_t(V)) x = uint32_t(V - 1);   // only after a barrier timeout
     const int owner = part_of(int(x >> 4), p.tiles, nwg);
-    const float z = __hip_atomic_load(&p.zpart[(size_t((kk & 1) * nwg + owner)) * B + b],
-                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float z;
+    if constexpr (SMALL && !GUMBEL)
+      z = key_value(key);   // the greedy key carries the logit itself
+    else if constexpr (SMALL)
+      z = small_logit(&p.wz[(size_t(kk - 1) * B + b) * nwg + owner], &p.ctrl[1], p.spin_limit);
+    else
+      z = __hip_atomic_load(&p.zpart[(size_t((kk & 1) * nwg + owner)) * B + b], __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
     if constexpr (STEP)   // read by the fused verify of another workgroup
       store_dev(&p.tokens[size_t(b) * gamma + kk - 1], int32_t(x));
     else
@@ -1028,7 +1104,19 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       const int rows = min(grs, B - g0);
 
       // tokens of step k-1 of this group are final once every workgroup has arrived
-      if (k > 1) grid_wait(bar(grp), &p.ctrl[1], unsigned(k - 1) * unsigned(nwg), p.spin_limit);
+      // (SMALL: once every workgroup's key of each request is there)
+      if constexpr (SMALL) {
+        if (k > 1) {
+          if (wave < rows) {
+            const uint64_t key =
+                small_max(&p.wkeys[(size_t(k - 2) * B + g0 + wave) * nwg], nwg, lane, &p.ctrl[1], p.spin_limit);
+            if (lane == 0) lds_sk[wave] = key;
+          }
+          __syncthreads();
+        }
+      } else if (k > 1) {
+        grid_wait(bar(grp), &p.ctrl[1], unsigned(k - 1) * unsigned(nwg), p.spin_limit);
+      }
 
       // 1. previous tokens of the group's rows
       uint64_t own_key = 0ull;   // key of step k-1 for a row this workgroup owns (emitted below)
@@ -1040,8 +1128,9 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
         if (k == 1) {
           x = min(max(int(p.anchor[b]), 0), V - 1);
         } else {
-          const uint64_t key = __hip_atomic_load(&p.slots[size_t(k - 2) * B + b], __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t key = SMALL ? lds_sk[tid]
+                                     : __hip_atomic_load(&p.slots[size_t(k - 2) * B + b], __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
           own_key = key;
           x = int(key_index(key));
           if (key == 0ull || x >= V || x < 0) x = V - 1;
@@ -1237,7 +1326,20 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       if (tid < rows) {
         const uint64_t key = lds_key[tid];
         lds_key[tid] = 0ull;
-        if (key != 0ull) {
+        if constexpr (SMALL) {
+          // every workgroup writes an entry (1, below any real key, when it has no candidate)
+          const size_t e = (size_t(k - 1) * B + g0 + tid) * nwg + wg;
+          if constexpr (GUMBEL) {
+            uint32_t zb = 1u;
+            if (key != 0ull) {
+              const int w = part_of(int(key_index(key) >> 4) - wg_lo, wg_nt, NW);
+              zb = ~__float_as_uint(lds_z[w][tid]);
+              zb = zb ? zb : 1u;
+            }
+            store_dev(&p.wz[e], zb);
+          }
+          store_dev(&p.wkeys[e], key != 0ull ? key : uint64_t(1));
+        } else if (key != 0ull) {
           const int b = g0 + tid;
           __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(&p.slots[size_t(k - 1) * B + b]),
                                  (unsigned long long)key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1247,7 +1349,9 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
         }
       }
       const bool last = (k == gamma) && (grp + 1 == ngroups);
-      if (ngroups == 1 || last) {
+      if constexpr (SMALL) {
+        __syncthreads();
+      } else if (ngroups == 1 || last) {
         grid_arrive(bar(grp));
       } else {
         pending = grp;
@@ -1261,12 +1365,23 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     }
   }
   // every group's last step is final before its outputs are read
-  for (int g = 0; g < ngroups; ++g) grid_wait(bar(g), &p.ctrl[1], unsigned(gamma) * unsigned(nwg), p.spin_limit);
+  if constexpr (SMALL) {
+    // wave w takes this workgroup's w-th owned request, wg + w * nwg (at most NW of them)
+    const int bw = wg + wave * nwg;
+    if (bw < B) {
+      const uint64_t key = small_max(&p.wkeys[(size_t(gamma - 1) * B + bw) * nwg], nwg, lane, &p.ctrl[1],
+                                     p.spin_limit);
+      if (lane == 0) lds_sk[wave] = key;
+    }
+    __syncthreads();
+  } else {
+    for (int g = 0; g < ngroups; ++g) grid_wait(bar(g), &p.ctrl[1], unsigned(gamma) * unsigned(nwg), p.spin_limit);
+  }
 
   // outputs of the last step; a failed synchronisation marks every token -1
   const bool failed = load_dev(&p.ctrl[1]) != 0u;
   for (int b = wg + tid * nwg; b < B; b += NT * nwg) {
-    const uint64_t key = load_dev(&p.slots[size_t(gamma - 1) * B + b]);
+    const uint64_t key = SMALL ? lds_sk[tid] : load_dev(&p.slots[size_t(gamma - 1) * B + b]);
     emit(b, gamma, key);
     if (failed)
       for (int kk = 0; kk < gamma; ++kk) {
@@ -1298,6 +1413,13 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
     __syncthreads();
     const long long nslots = (long long)gamma * B;
     for (long long i = tid; i < nslots; i += NT) store_dev(&p.slots[i], uint64_t(0));
+    if constexpr (SMALL) {
+      const long long nw = nslots * nwg;
+      for (long long i = tid; i < nw; i += NT) {
+        store_dev(&p.wkeys[i], uint64_t(0));
+        if constexpr (GUMBEL) store_dev(&p.wz[i], 0u);
+      }
+    }
     for (int g = tid; g < ngroups; g += NT) store_dev(bar(g), 0u);
     if (tid == 0) {
       store_dev(&p.ctrl[1], 0u);
@@ -1315,9 +1437,27 @@ struct KernelChoice {
 constexpr int kDraftWaves = 8;
 
 template <bool BF16, int R, bool G, bool RNN>
-KernelChoice pick_r(bool full, int tiles_per_wave, bool step) {
+KernelChoice pick_r(bool full, int tiles_per_wave, bool step, bool small) {
   constexpr int NW = kDraftWaves, GR = kMaxGroupRows;
   constexpr int TPW = BF16 ? 5 : 4;
+  // small batches: the SMALL instances (bf16 at rank 256, fp32 at rank 16)
+  if constexpr (!RNN && ((BF16 && R == 256) || (!BF16 && R == 16))) {
+    if (small) {   // (never with the fused step)
+      if constexpr (BF16) {
+        if (full && tiles_per_wave <= 4)
+          return KernelChoice{
+              reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, 4, GR, G, true, RNN, false, true>),
+              NW * 64, 4};
+        if (full)
+          return KernelChoice{
+              reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, true, RNN, false, true>),
+              NW * 64, TPW};
+      }
+      return KernelChoice{
+          reinterpret_cast<const void*>(&markov_draft_kernel<BF16, R, NW, TPW, GR, G, false, RNN, false, true>),
+          NW * 64, TPW};
+    }
+  }
   if constexpr (BF16 && R == 256 && !RNN) {
     // the fused draft-schedule-verify step (whole tiles only)
     if (step && full) {
@@ -1345,25 +1485,29 @@ KernelChoice pick_r(bool full, int tiles_per_wave, bool step) {
 }
 
 template <bool G>
-bool pick(bool bf16, int r, bool full, bool rnn, int tpw_need, KernelChoice* out, bool step = false) {
+bool pick(bool bf16, int r, bool full, bool rnn, int tpw_need, KernelChoice* out, bool step = false,
+          bool small = false) {
   const int n = tpw_need;
   if (bf16) {
     switch (r) {
-      case 32: *out = rnn ? pick_r<true, 32, G, true>(full, n, false) : pick_r<true, 32, G, false>(full, n, false); return true;
-      case 64: *out = rnn ? pick_r<true, 64, G, true>(full, n, false) : pick_r<true, 64, G, false>(full, n, false); return true;
-      case 128: *out = rnn ? pick_r<true, 128, G, true>(full, n, false) : pick_r<true, 128, G, false>(full, n, false); return true;
-      case 256: *out = rnn ? pick_r<true, 256, G, true>(full, n, false) : pick_r<true, 256, G, false>(full, n, step); return true;
+      case 32: *out = rnn ? pick_r<true, 32, G, true>(full, n, false, false) : pick_r<true, 32, G, false>(full, n, false, false); return true;
+      case 64: *out = rnn ? pick_r<true, 64, G, true>(full, n, false, false) : pick_r<true, 64, G, false>(full, n, false, false); return true;
+      case 128: *out = rnn ? pick_r<true, 128, G, true>(full, n, false, false) : pick_r<true, 128, G, false>(full, n, false, false); return true;
+      case 256: *out = rnn ? pick_r<true, 256, G, true>(full, n, false, false) : pick_r<true, 256, G, false>(full, n, step, small); return true;
       default: return false;
     }
   }
   if (rnn) return false;
   switch (r) {
-    case 16: *out = pick_r<false, 16, G, false>(full, n, false); return true;
-    case 32: *out = pick_r<false, 32, G, false>(full, n, false); return true;
-    case 64: *out = pick_r<false, 64, G, false>(full, n, false); return true;
+    case 16: *out = pick_r<false, 16, G, false>(full, n, false, small); return true;
+    case 32: *out = pick_r<false, 32, G, false>(full, n, false, false); return true;
+    case 64: *out = pick_r<false, 64, G, false>(full, n, false, false); return true;
     default: return false;
   }
 }
+
+// whether pick() has SMALL instances for this shape
+inline bool small_kernel_exists(bool bf16, int r, bool rnn) { return !rnn && (bf16 ? r == 256 : r == 16); }
 
 // Scratch of the allocation-free entry point (dspark_markov_draft_noalloc):
 // the draft workspace as a file-scope device array, one copy per GPU for the
@@ -1412,6 +1556,11 @@ DraftWorkspace draft_workspace_layout(int B, int gamma, int r_state) {
   off = align256(off + size_t((B + 15) / 16) * kBarStride * sizeof(unsigned int));
   w.slots = off;
   off = align256(off + size_t(gamma) * B * sizeof(uint64_t));
+  const size_t small_entries = (B <= kSmallBatch) ? size_t(gamma) * B * kMaxDraftWorkgroups : 0;
+  w.wkeys = off;
+  off = align256(off + small_entries * sizeof(uint64_t));
+  w.wz = off;
+  off = align256(off + small_entries * sizeof(uint32_t));
   w.zpart = off;
   off = align256(off + size_t(2) * kMaxDraftWorkgroups * B * sizeof(float));
   w.hdot = off;
@@ -1427,7 +1576,10 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   if (fused) *fused = false;
   KernelChoice kc;
   const bool rnn = a.decay != nullptr;
-  if (!(a.gumbel ? pick<true>(a.bf16, a.r, false, rnn, 0, &kc) : pick<false>(a.bf16, a.r, false, rnn, 0, &kc))) {
+  // small batches synchronise through per-workgroup winner keys (SMALL kernels)
+  const bool small = a.B <= kSmallBatch && small_kernel_exists(a.bf16, a.r, rnn);
+  if (!(a.gumbel ? pick<true>(a.bf16, a.r, false, rnn, 0, &kc, false, small)
+                 : pick<false>(a.bf16, a.r, false, rnn, 0, &kc, false, small))) {
     *unsupported = rnn ? "the RNN head supports bf16 storage with r in {32, 64, 128, 256}"
                        : a.bf16 ? "bf16 drafting supports r in {32, 64, 128, 256}"
                                 : "fp32 drafting supports r in {16, 32, 64}";
@@ -1448,17 +1600,19 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   // workgroups must fit in the draft grid, and the last one's verify follows.
   // Larger batches take three launches: their drafting kernel is bandwidth
   // bound, and the fused kernel's extra registers slow its tile loop by about
-  // as much as the two launches it saves.
+  // as much as the two launches it saves.  So do small batches: their
+  // drafting kernel has no per-step barrier, and the fused tail's barrier and
+  // ranking cost more than the two launch gaps.
   const long long n_items = (long long)a.B * a.gamma;
   const int sched_e = n_items <= kRankThreads ? 1 : 2;
-  const bool step = a.step != nullptr && full && a.bf16 && a.r == 256 && !rnn && !a.noalloc &&
+  const bool step = a.step != nullptr && full && a.bf16 && a.r == 256 && !rnn && !a.noalloc && !small &&
                     n_items <= kFusedStepItems && (n_items + 15) / 16 <= nwg;
   if (full) {
     const int tpw_need = (per_wg + kDraftWaves - 1) / kDraftWaves;   // most tiles any wave owns
     if (a.gumbel)
-      pick<true>(a.bf16, a.r, true, rnn, tpw_need, &kc, step);
+      pick<true>(a.bf16, a.r, true, rnn, tpw_need, &kc, step, small);
     else
-      pick<false>(a.bf16, a.r, true, rnn, tpw_need, &kc, step);
+      pick<false>(a.bf16, a.r, true, rnn, tpw_need, &kc, step, small);
   }
   const int nwaves = kc.threads / 64;
   if ((per_wg + nwaves - 1) / nwaves > kc.tpw) {
@@ -1477,8 +1631,8 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
       return hipSuccess;
     }
     void* sp = nullptr;
-    // the counters and arg-max slots of this shape: [0, end of the slots)
-    const size_t zero_bytes = L.slots + size_t(a.gamma) * a.B * sizeof(uint64_t);
+    // the sections that must start at zero for this shape: [0, zpart)
+    const size_t zero_bytes = L.zpart;
     e = noalloc_scratch(stream, &sp, (uint64_t(uint32_t(a.B)) << 32) | uint32_t(a.gamma), zero_bytes);
     if (e != hipSuccess) return e;
     ws = static_cast<char*>(sp);
@@ -1518,6 +1672,8 @@ hipError_t launch_markov_draft(const DraftArgs& a, hipStream_t stream, const cha
   p.hdot = reinterpret_cast<double*>(ws + L.hdot);
   p.decay = a.decay;
   p.state = rnn ? reinterpret_cast<uint16_t*>(ws + L.state) : nullptr;
+  p.wkeys = reinterpret_cast<uint64_t*>(ws + L.wkeys);
+  p.wz = reinterpret_cast<uint32_t*>(ws + L.wz);
   p.sched_tickets = nullptr;
   p.sched_sorted = nullptr;
   p.t_step = nullptr;

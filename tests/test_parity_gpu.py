@@ -124,6 +124,30 @@ def test_small_gumbel(shape):
     end_to_end(w, d, out)
 
 
+# Batches of at most 8 requests synchronise the draft positions through each
+# workgroup's winner keys instead of arrival counters (bf16 at rank 256, fp32
+# at rank 16): every kernel instance of that path, both samplings.
+SMALL_BATCH = [
+    (dict(B=3, gamma=5, V=3001, r=256, d=24, dtype="bf16"), "greedy"),       # guarded kernel, ragged tile
+    (dict(B=1, gamma=6, V=3001, r=256, d=8, dtype="bf16"), "gumbel"),
+    (dict(B=8, gamma=4, V=65536, r=256, d=16, dtype="bf16"), "greedy"),      # whole tiles, four slots; largest B
+    (dict(B=4, gamma=4, V=70016, r=256, d=16, dtype="bf16"), "gumbel"),
+    (dict(B=2, gamma=3, V=151936, r=256, d=16, dtype="bf16"), "gumbel"),     # five slots
+    (dict(B=2, gamma=3, V=777, r=16, d=8, dtype="f32"), "greedy"),
+    (dict(B=3, gamma=4, V=1030, r=16, d=12, dtype="f32"), "gumbel"),
+]
+
+
+@pytest.mark.parametrize("shape,sampling", SMALL_BATCH,
+                         ids=lambda v: "x".join(str(x) for x in v.values()) if isinstance(v, dict) else v)
+def test_small_batch(shape, sampling):
+    w = wl.make_workload(wl.small_config(sampling=sampling, **shape))
+    if sampling == "gumbel":
+        w["seed"] = 0x5EED0001
+    d, out = run_case(w)
+    end_to_end(w, d, out)
+
+
 @pytest.mark.parametrize("V,sampling", [(70016, "greedy"), (100000, "greedy"), (131072, "greedy"),
                                         (100000, "gumbel"), (140000, "greedy"), (140000, "gumbel")])
 def test_vocab_splits_of_the_whole_tile_path(V, sampling):

@@ -1,6 +1,6 @@
 """dspark_step (draft, schedule and verify in one call) against the three
 calls it chains, made in order on the same inputs: every output bit for bit.
-Whole-tile bf16 rank-256 shapes with B*gamma <= 1024 run as one launch
+Whole-tile bf16 rank-256 shapes with 8 < B and B*gamma <= 1024 run as one launch
 (after the last draft position the scheduler's ranking workgroups, then the
 verify, in the same kernel); the others as three launches.  The three calls themselves are
 compared with the oracle by the parity tests; here the oracle also re-derives
@@ -74,9 +74,9 @@ def compare(d, label, repeats=2):
 CASES = {
     "whole-tile greedy": dict(B=96, gamma=6, V=69632, r=256, d=48, dtype="bf16"),
     "whole-tile gumbel": dict(B=40, gamma=16, V=65536, r=256, d=32, dtype="bf16", sampling="gumbel"),
-    "one request": dict(B=1, gamma=8, V=65536, r=256, d=32, dtype="bf16"),
+    "one request": dict(B=1, gamma=8, V=65536, r=256, d=32, dtype="bf16"),   # small batch: three launches
     "fused limit, two keys per thread": dict(B=64, gamma=16, V=65536, r=256, d=32, dtype="bf16"),
-    "five slots per wave, gumbel": dict(B=8, gamma=16, V=151936, r=256, d=32, dtype="bf16", sampling="gumbel"),
+    "five slots per wave, gumbel": dict(B=9, gamma=16, V=151936, r=256, d=32, dtype="bf16", sampling="gumbel"),
     "above the fused limit": dict(B=65, gamma=16, V=65536, r=256, d=32, dtype="bf16"),
     "three launches, bf16 r=32": dict(B=10, gamma=3, V=3001, r=32, d=20, dtype="bf16", sampling="gumbel"),
     "three launches, fp32": dict(B=5, gamma=4, V=1030, r=16, d=12, dtype="f32"),
@@ -96,8 +96,9 @@ def test_step_equals_three_calls(name, launch):
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4])
 def test_step_full_size(cid):
-    """The full-size workloads: B*gamma = 8 and 1024 (one launch), 4096 and
-    8192 (three launches; the last with Gumbel-max sampling)."""
+    """The full-size workloads: B = 1 (three launches, the small-batch
+    drafting kernel), B*gamma = 1024 (one launch), 4096 and 8192 (three
+    launches; the last with Gumbel-max sampling)."""
     w = wl.make_workload(wl.WORKLOADS[cid])
     say(f"[case] step full size config {cid}")
     binding.set_draft_launch("exclusive")
