@@ -118,7 +118,9 @@ size_t dspark_rnn_draft_workspace_bytes(int B, int gamma, int V, int r);
  *                 256-byte aligned, zero-filled (e.g. hipMemsetAsync) before
  *                 its first use and before any call whose B or gamma differs
  *                 from the previous call's on it: its counters and arg-max
- *                 slots sit at offsets that depend on B and gamma.  A call
+ *                 slots (for B <= 8 also every workgroup's winner keys, up
+ *                 to gamma * B * 512 * 12 bytes) sit at offsets that depend
+ *                 on B and gamma.  A call
  *                 leaves them zero again, so calls of the same B and gamma
  *                 reuse it without clearing.  A workspace found dirty by the
  *                 barrier check is cleaned by the call, whose tokens are then
