@@ -788,7 +788,7 @@ template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL, boo
           bool SMALL = false>
 __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p) {
   static_assert(!STEP || (FULL && !RNN && NW * 64 == kRankThreads), "the fused step runs on the whole-tile kernel");
-  static_assert(!SMALL || (!RNN && !STEP && kSmallBatch <= NW && kSmallBatch <= 16),
+  static_assert(!SMALL || (!STEP && kSmallBatch <= NW && kSmallBatch <= 16),
                 "one wave per request of one group; no fused step");
   static_assert(!RNN || BF16, "the RNN head is built for bf16 storage");
   typedef Elem<BF16> E;
@@ -1320,6 +1320,10 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
         }
       }
 
+      // (SMALL RNN head: the owners' state stores of this unit complete
+      // before any key of it is stored, so a reader that has every key of
+      // the step also reads the states)
+      if constexpr (SMALL && RNN) wait_vmem();
       __syncthreads();
 
       // 5. publish this workgroup's winner of every row of the group
@@ -1440,8 +1444,8 @@ template <bool BF16, int R, bool G, bool RNN>
 KernelChoice pick_r(bool full, int tiles_per_wave, bool step, bool small) {
   constexpr int NW = kDraftWaves, GR = kMaxGroupRows;
   constexpr int TPW = BF16 ? 5 : 4;
-  // small batches: the SMALL instances (bf16 at rank 256, fp32 at rank 16)
-  if constexpr (!RNN && ((BF16 && R == 256) || (!BF16 && R == 16))) {
+  // small batches: the SMALL instances (bf16 at rank 256, both heads; fp32 at rank 16)
+  if constexpr ((BF16 && R == 256) || (!BF16 && R == 16 && !RNN)) {
     if (small) {   // (never with the fused step)
       if constexpr (BF16) {
         if (full && tiles_per_wave <= 4)
@@ -1493,7 +1497,7 @@ bool pick(bool bf16, int r, bool full, bool rnn, int tpw_need, KernelChoice* out
       case 32: *out = rnn ? pick_r<true, 32, G, true>(full, n, false, false) : pick_r<true, 32, G, false>(full, n, false, false); return true;
       case 64: *out = rnn ? pick_r<true, 64, G, true>(full, n, false, false) : pick_r<true, 64, G, false>(full, n, false, false); return true;
       case 128: *out = rnn ? pick_r<true, 128, G, true>(full, n, false, false) : pick_r<true, 128, G, false>(full, n, false, false); return true;
-      case 256: *out = rnn ? pick_r<true, 256, G, true>(full, n, false, false) : pick_r<true, 256, G, false>(full, n, step, small); return true;
+      case 256: *out = rnn ? pick_r<true, 256, G, true>(full, n, false, small) : pick_r<true, 256, G, false>(full, n, step, small); return true;
       default: return false;
     }
   }
@@ -1507,7 +1511,7 @@ bool pick(bool bf16, int r, bool full, bool rnn, int tpw_need, KernelChoice* out
 }
 
 // whether pick() has SMALL instances for this shape
-inline bool small_kernel_exists(bool bf16, int r, bool rnn) { return !rnn && (bf16 ? r == 256 : r == 16); }
+inline bool small_kernel_exists(bool bf16, int r, bool rnn) { return bf16 ? r == 256 : (r == 16 && !rnn); }
 
 // Scratch of the allocation-free entry point (dspark_markov_draft_noalloc):
 // the draft workspace as a file-scope device array, one copy per GPU for the

@@ -49,6 +49,10 @@ CASES = [
     (256, 2, 151936, 256, 32, "gumbel"),      # whole-tile kernel, two full groups, Gumbel-max
     (17, 3, 69648, 64, 16, "greedy"),         # whole-tile kernel, rank 64, ragged single group
     (140, 3, 69632, 256, 0, "greedy"),        # whole-tile kernel without a hidden state (d = 0)
+    # batches of at most 8 requests (rank 256): synchronised through the winner keys
+    (4, 5, 70016, 256, 32, "gumbel"),         # whole tiles, four slots
+    (2, 3, 3001, 256, 16, "greedy"),          # guarded kernel
+    (8, 4, 65536, 256, 16, "greedy"),         # the largest such batch
 ]
 
 
@@ -70,7 +74,7 @@ def test_rnn_draft_parity(B, gamma, V, r, d, sampling):
     assert (np.diff(surv, axis=1) <= 0).all()
 
 
-@pytest.mark.parametrize("B,gamma,V,r", [(40, 6, 3000, 64), (140, 4, 69632, 256)])
+@pytest.mark.parametrize("B,gamma,V,r", [(40, 6, 3000, 64), (140, 4, 69632, 256), (3, 5, 65536, 256)])
 def test_zero_decay_equals_markov_kernel(B, gamma, V, r):
     cfg = wl.small_config(B=B, gamma=gamma, V=V, r=r, d=32, dtype="bf16")
     w = wl.make_workload(cfg)
