@@ -118,7 +118,7 @@ size_t dspark_rnn_draft_workspace_bytes(int B, int gamma, int V, int r);
  *                 256-byte aligned, zero-filled (e.g. hipMemsetAsync) before
  *                 its first use and before any call whose B or gamma differs
  *                 from the previous call's on it: its counters and arg-max
- *                 slots (for B <= 8 also every workgroup's winner keys, up
+ *                 slots (for B <= 16 also every workgroup's winner keys, up
  *                 to gamma * B * 512 * 12 bytes) sit at offsets that depend
  *                 on B and gamma.  A call
  *                 leaves them zero again, so calls of the same B and gamma
@@ -459,7 +459,7 @@ dspark_status dspark_schedule_threshold(
  *              aligned: the drafting workspace, then the scheduler's, zero-filled
  *              as dspark_serve's (before the first use and on a change of B or
  *              gamma).
- * For bf16 storage at r = 256 on the whole-tile path with 8 < B and
+ * For bf16 storage at r = 256 on the whole-tile path with 16 < B and
  * B * gamma <= 1024, the three run in one launch: after the last draft position every workgroup
  * ranks its share of the survivals, and the workgroup that finishes last runs
  * the scheduler's remaining steps and the verify (this saves the two launch

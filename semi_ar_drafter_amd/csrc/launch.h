@@ -13,9 +13,10 @@ constexpr int kMaxDraftWorkgroups = 512;
 constexpr int kMaxOwnedRows = 64;
 // Requests per group in the draft kernel (LDS holds one group's embeddings).
 constexpr int kMaxGroupRows = 128;
-// Batches of at most this many requests synchronise the draft positions
-// through per-workgroup winner keys instead of arrival counters.
-constexpr int kSmallBatch = 8;
+// Batches of at most this many requests (one group of at most 16 rows)
+// synchronise the draft positions through per-workgroup winner keys instead
+// of arrival counters.
+constexpr int kSmallBatch = 16;
 // Distance (in 32-bit words) between the per-group arrival counters (one
 // 128-byte line each: every workgroup polls them).
 constexpr int kBarStride = 32;

@@ -788,8 +788,8 @@ template <bool BF16, int R, int NW, int TPW, int GR, bool GUMBEL, bool FULL, boo
           bool SMALL = false>
 __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p) {
   static_assert(!STEP || (FULL && !RNN && NW * 64 == kRankThreads), "the fused step runs on the whole-tile kernel");
-  static_assert(!SMALL || (!STEP && kSmallBatch <= NW && kSmallBatch <= 16),
-                "one wave per request of one group; no fused step");
+  static_assert(!SMALL || (!STEP && kSmallBatch <= 2 * NW && kSmallBatch <= 16),
+                "at most two requests per wave, one group; no fused step");
   static_assert(!RNN || BF16, "the RNN head is built for bf16 storage");
   typedef Elem<BF16> E;
   typedef typename E::store_t st_t;
@@ -814,7 +814,7 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   __shared__ uint64_t lds_key[GR];
   __shared__ float lds_z[NW][GR];
   __shared__ int lds_x[GR];
-  __shared__ uint64_t lds_sk[SMALL ? NW : 1];   // SMALL: the previous step's key of each request
+  __shared__ uint64_t lds_sk[SMALL ? 2 * NW : 1];   // SMALL: the previous step's key of each request
   __shared__ double lds_hd[GR];
   __shared__ float lds_S[kMaxOwnedRows];
   __shared__ float lds_we[R];   // confidence weights of the Markov-embedding half
@@ -1107,10 +1107,16 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
       // (SMALL: once every workgroup's key of each request is there)
       if constexpr (SMALL) {
         if (k > 1) {
+          // wave w takes rows w and w + NW
           if (wave < rows) {
             const uint64_t key =
                 small_max(&p.wkeys[(size_t(k - 2) * B + g0 + wave) * nwg], nwg, lane, &p.ctrl[1], p.spin_limit);
             if (lane == 0) lds_sk[wave] = key;
+          }
+          if (wave + NW < rows) {
+            const uint64_t key = small_max(&p.wkeys[(size_t(k - 2) * B + g0 + wave + NW) * nwg], nwg, lane,
+                                           &p.ctrl[1], p.spin_limit);
+            if (lane == 0) lds_sk[wave + NW] = key;
           }
           __syncthreads();
         }
@@ -1370,12 +1376,16 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   }
   // every group's last step is final before its outputs are read
   if constexpr (SMALL) {
-    // wave w takes this workgroup's w-th owned request, wg + w * nwg (at most NW of them)
-    const int bw = wg + wave * nwg;
-    if (bw < B) {
-      const uint64_t key = small_max(&p.wkeys[(size_t(gamma - 1) * B + bw) * nwg], nwg, lane, &p.ctrl[1],
-                                     p.spin_limit);
-      if (lane == 0) lds_sk[wave] = key;
+    // wave w takes this workgroup's owned requests number w and w + NW,
+    // wg + w * nwg and wg + (w + NW) * nwg
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int bw = wg + (wave + h * NW) * nwg;
+      if (bw < B) {
+        const uint64_t key = small_max(&p.wkeys[(size_t(gamma - 1) * B + bw) * nwg], nwg, lane, &p.ctrl[1],
+                                       p.spin_limit);
+        if (lane == 0) lds_sk[wave + h * NW] = key;
+      }
     }
     __syncthreads();
   } else {

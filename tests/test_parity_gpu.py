@@ -124,9 +124,10 @@ def test_small_gumbel(shape):
     end_to_end(w, d, out)
 
 
-# Batches of at most 8 requests synchronise the draft positions through each
+# Batches of at most 16 requests synchronise the draft positions through each
 # workgroup's winner keys instead of arrival counters (bf16 at rank 256, fp32
-# at rank 16): every kernel instance of that path, both samplings.
+# at rank 16): every kernel instance of that path, both samplings, one and two
+# requests per wave.
 SMALL_BATCH = [
     (dict(B=3, gamma=5, V=3001, r=256, d=24, dtype="bf16"), "greedy"),       # guarded kernel, ragged tile
     (dict(B=1, gamma=6, V=3001, r=256, d=8, dtype="bf16"), "gumbel"),
@@ -135,6 +136,10 @@ SMALL_BATCH = [
     (dict(B=2, gamma=3, V=151936, r=256, d=16, dtype="bf16"), "gumbel"),     # five slots
     (dict(B=2, gamma=3, V=777, r=16, d=8, dtype="f32"), "greedy"),
     (dict(B=3, gamma=4, V=1030, r=16, d=12, dtype="f32"), "gumbel"),
+    (dict(B=16, gamma=4, V=65536, r=256, d=16, dtype="bf16"), "greedy"),     # two requests per wave; largest B
+    (dict(B=12, gamma=3, V=5003, r=256, d=16, dtype="bf16"), "gumbel"),
+    (dict(B=9, gamma=3, V=151936, r=256, d=16, dtype="bf16"), "greedy"),
+    (dict(B=16, gamma=3, V=2000, r=16, d=8, dtype="f32"), "greedy"),
 ]
 
 

@@ -49,10 +49,11 @@ CASES = [
     (256, 2, 151936, 256, 32, "gumbel"),      # whole-tile kernel, two full groups, Gumbel-max
     (17, 3, 69648, 64, 16, "greedy"),         # whole-tile kernel, rank 64, ragged single group
     (140, 3, 69632, 256, 0, "greedy"),        # whole-tile kernel without a hidden state (d = 0)
-    # batches of at most 8 requests (rank 256): synchronised through the winner keys
+    # batches of at most 16 requests (rank 256): synchronised through the winner keys
     (4, 5, 70016, 256, 32, "gumbel"),         # whole tiles, four slots
     (2, 3, 3001, 256, 16, "greedy"),          # guarded kernel
-    (8, 4, 65536, 256, 16, "greedy"),         # the largest such batch
+    (8, 4, 65536, 256, 16, "greedy"),
+    (16, 3, 65536, 256, 16, "gumbel"),        # the largest such batch: two requests per wave
 ]
 
 

@@ -1,6 +1,6 @@
 """dspark_step (draft, schedule and verify in one call) against the three
 calls it chains, made in order on the same inputs: every output bit for bit.
-Whole-tile bf16 rank-256 shapes with 8 < B and B*gamma <= 1024 run as one launch
+Whole-tile bf16 rank-256 shapes with 16 < B and B*gamma <= 1024 run as one launch
 (after the last draft position the scheduler's ranking workgroups, then the
 verify, in the same kernel); the others as three launches.  The three calls themselves are
 compared with the oracle by the parity tests; here the oracle also re-derives
@@ -76,7 +76,7 @@ CASES = {
     "whole-tile gumbel": dict(B=40, gamma=16, V=65536, r=256, d=32, dtype="bf16", sampling="gumbel"),
     "one request": dict(B=1, gamma=8, V=65536, r=256, d=32, dtype="bf16"),   # small batch: three launches
     "fused limit, two keys per thread": dict(B=64, gamma=16, V=65536, r=256, d=32, dtype="bf16"),
-    "five slots per wave, gumbel": dict(B=9, gamma=16, V=151936, r=256, d=32, dtype="bf16", sampling="gumbel"),
+    "five slots per wave, gumbel": dict(B=17, gamma=16, V=151936, r=256, d=32, dtype="bf16", sampling="gumbel"),
     "above the fused limit": dict(B=65, gamma=16, V=65536, r=256, d=32, dtype="bf16"),
     "three launches, bf16 r=32": dict(B=10, gamma=3, V=3001, r=32, d=20, dtype="bf16", sampling="gumbel"),
     "three launches, fp32": dict(B=5, gamma=4, V=1030, r=16, d=12, dtype="f32"),
