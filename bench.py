@@ -52,6 +52,9 @@ VALU_PEAK_GOPS = 256 * 64 * 2.4
 # y - p (1); rounding to 2^-32 (2); bin index (3); histogram address (1);
 # histogram add (1).
 STS_OPS_PER_EVAL = 34
+# operations the fit needs per evaluation whatever the implementation, the
+# exponential and the reciprocal counted as one each
+STS_ALG_OPS_PER_EVAL = 8
 SETTLE_S = 0.2   # untimed steps before the warm-up: long enough for the clocks to settle
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # the draft kernel's device code (the traffic summary is tied to these files)
@@ -183,10 +186,19 @@ def time_sts_fit(torch, wl, sts_fit, reps: int = 10):
     us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)[reps // 2]
     evals = c.N * c.gamma * c.G
     gops = evals * STS_OPS_PER_EVAL / (us / 1e6) / 1e9
+    # the same rate against the operations the fit cannot do without, each
+    # counted once (the fp64 exponential and reciprocal as one operation each)
+    alg_gops = evals * STS_ALG_OPS_PER_EVAL / (us / 1e6) / 1e9
     return {"workload": f"calibration N={c.N} gamma={c.gamma} G={c.G} bins={c.n_bins}",
             "us_per_fit": round(us, 1), "evals_per_s": round(evals / (us / 1e6), 1),
             "roofline": {"bound": "alu", "achieved": round(gops, 1), "peak": VALU_PEAK_GOPS, "unit": "Gop/s",
                          "frac": round(gops / VALU_PEAK_GOPS, 4), "ops_per_eval": STS_OPS_PER_EVAL,
+                         "ops_note": "operations of this implementation (its exponential is 18 of them): frac is "
+                                     "the fraction of the VALU issue rate its instruction stream reaches",
+                         "algorithmic_ops_per_eval": STS_ALG_OPS_PER_EVAL,
+                         "frac_algorithmic": round(alg_gops / VALU_PEAK_GOPS, 4),
+                         "algorithmic_note": "scale, exponential, 1 + e, reciprocal, S * sigma, y - p, bin, "
+                                             "histogram add: one operation each",
                          "kernel": f"sts_pass_kernel ({c.gamma} launches + 1 clear per fit)"}}
 
 
