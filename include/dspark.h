@@ -123,8 +123,9 @@ size_t dspark_rnn_draft_workspace_bytes(int B, int gamma, int V, int r);
  *                 on B and gamma.  A call
  *                 leaves them zero again, so calls of the same B and gamma
  *                 reuse it without clearing.  A workspace found dirty by the
- *                 barrier check is cleaned by the call, whose tokens are then
- *                 all -1 (stale arg-max slots are not detected).
+ *                 barrier check (for B <= 16: a non-zero winner key of the
+ *                 first position) is cleaned by the call, whose tokens are
+ *                 then all -1 (stale arg-max slots are not detected).
  * The call is one kernel launch.  If the kernel cannot synchronise its
  * workgroups (it never can deadlock: its waits are bounded) every token of
  * the call is -1.

@@ -839,6 +839,10 @@ __global__ __launch_bounds__(NW * 64, 1) void markov_draft_kernel(DraftParams p)
   // A workspace left by a completed call has zero barrier counters; before
   // this workgroup's first arrival at most nwg - 1 others can have arrived.
   if (tid == 0 && load_dev(&p.bar[0]) >= unsigned(nwg)) store_dev(&p.ctrl[1], 2u);
+  // (SMALL: likewise its winner keys are all zero; this workgroup's entry of
+  // the first position and request is written by it alone, after this read)
+  if constexpr (SMALL)
+    if (tid == 0 && load_dev(&p.wkeys[wg]) != 0ull) store_dev(&p.ctrl[1], 2u);
 
   // hdot for every (owned request, position): one (b, k) per wave at a time.
   if constexpr (!FULL) {

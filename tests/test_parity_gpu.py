@@ -435,3 +435,24 @@ def test_dirty_workspace_is_flagged_and_cleaned():
     torch.cuda.synchronize()
     st = check_draft(w, tuple(x.cpu().numpy() for x in out))
     assert st.ok(), st
+
+
+def test_dirty_small_batch_workspace_is_flagged_and_cleaned():
+    """Batches of at most 16 requests do not use the barrier counters: stale
+    winner keys are what is detected.  The control words and the counters
+    (the first 512 bytes for such a batch) are left clean and everything
+    after them dirty: the call returns all -1 and leaves the workspace clean."""
+    from semi_ar_drafter_amd import binding, markov_draft
+    w = wl.make_workload(wl.small_config(B=3, gamma=3, V=3001, r=256, d=16, dtype="bf16"))
+    d = to_device(w)
+    nb = binding.workspace_bytes(3, 3, 3001, 256)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    ws[:512] = 0
+    args = (d["anchor"], d["U"], d["h"], d["W1"], d["W2"], d["conf_w"], d["conf_b"], d["sts_T"])
+    tok, _, _, _ = markov_draft(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert (tok.cpu().numpy() == -1).all()
+    out = markov_draft(*args, workspace=ws)
+    torch.cuda.synchronize()
+    st = check_draft(w, tuple(x.cpu().numpy() for x in out))
+    assert st.ok(), st
