@@ -140,6 +140,9 @@ SMALL_BATCH = [
     (dict(B=12, gamma=3, V=5003, r=256, d=16, dtype="bf16"), "gumbel"),
     (dict(B=9, gamma=3, V=151936, r=256, d=16, dtype="bf16"), "greedy"),
     (dict(B=16, gamma=3, V=2000, r=16, d=8, dtype="f32"), "greedy"),
+    # tiny vocabularies: one workgroup owning every request, ten owning up to two each
+    (dict(B=16, gamma=3, V=16, r=16, d=8, dtype="f32"), "greedy"),
+    (dict(B=16, gamma=2, V=160, r=256, d=8, dtype="bf16"), "gumbel"),
 ]
 
 
