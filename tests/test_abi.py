@@ -127,6 +127,17 @@ def test_workspace_size(lib):
     assert a % 256 == 0 and b % 256 == 0 and b > a > 256 * 16 * 8
 
 
+def test_small_batch_workspace_holds_the_winner_keys(lib):
+    """Batches of at most 16 requests also carve every workgroup's winner key
+    (8 bytes) and Gumbel logit (4 bytes) per position and request, for up to
+    512 workgroups; larger batches do not."""
+    for B, gamma in ((1, 8), (16, 64)):
+        n = lib.dspark_draft_workspace_bytes(B, gamma, 151936, 256)
+        assert n % 256 == 0 and n >= gamma * B * 512 * 12
+        assert n <= 8 << 20   # within the allocation-free entry point's scratch
+    assert lib.dspark_draft_workspace_bytes(17, 64, 151936, 256) < 17 * 64 * 512 * 12
+
+
 def sched(lib, B=4, gamma=4, n_min=4, n_count=17, surv=P, t=P, lens=P, m=P, ws=NULL, ws_bytes=0):
     return lib.dspark_schedule(B, gamma, surv, t, n_min, n_count, lens, m, NULL, ws, ctypes.c_size_t(ws_bytes),
                                NULL)
