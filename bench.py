@@ -29,7 +29,9 @@ confidence temperatures on 262144 synthetic calibration blocks, 128 candidate
 temperatures, 15 bins), also outside the step, against the VALU issue rate;
 `serve` runs dspark_serve (4 chained iterations of the same batch, anchors
 taken from the previous bonus tokens) under each verify-length policy;
-`rnn_head` times dspark_rnn_draft (the RNN sequential head) on the same inputs.
+`rnn_head` times dspark_rnn_draft (the RNN sequential head) on the same inputs;
+`latency_case` times the one-request, gamma = 8 workload (the draft call, and
+the whole step as one dspark_step call).
 """
 from __future__ import annotations
 
@@ -255,6 +257,42 @@ def time_serve(torch, serve, w, anchor, U, h, W1, W2, conf_w, sts_T, target, t_s
     return res
 
 
+def time_latency_case(torch, wl, dev, markov_draft, step, reps: int = 3, calls: int = 20):
+    """The latency workload (one request, gamma = 8, V = 151936): the draft
+    call and the whole step in one dspark_step call (events around `calls`
+    back-to-back calls, best of `reps`), inputs resident in HBM."""
+    c = wl.WORKLOADS[1]
+    w = wl.make_workload(c)
+    anchor, U, h, W1, W2 = dev(w["anchor"]), dev(w["U"]), dev(w["h"]), dev(w["W1"]), dev(w["W2"])
+    conf_w, sts_T, target, t_step = dev(w["conf_w"]), dev(w["sts_T"]), dev(w["target"]), dev(w["t_step"])
+    args = (anchor, U, h, W1, W2, conf_w, w["conf_b"], sts_T)
+
+    def best(fn):
+        t = []
+        for _ in range(reps):
+            for _ in range(3):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(calls):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b) * 1e3 / calls)
+        return min(t)
+
+    draft_us = best(lambda: markov_draft(*args, mode=c.sampling, seed=w["seed"]))
+    step_us = best(lambda: step(*args, target, t_step, w["n_min"], mode=c.sampling, seed=w["seed"]))
+    tok = step(*args, target, t_step, w["n_min"], mode=c.sampling, seed=w["seed"])[0].cpu().numpy()
+    return {"workload": f"B={c.B} gamma={c.gamma} V={c.V} r={c.r} d={c.d} {c.dtype} {c.sampling}",
+            "draft_us": round(draft_us, 2), "step_us": round(step_us, 2),
+            "drafted_tokens_per_s": round(c.B * c.gamma / (step_us / 1e6), 1),
+            "outputs_valid": bool(((tok >= 0) & (tok < c.V)).all()),
+            "note": "batches of at most 16 requests synchronise the draft positions through the workgroups' "
+                    "winner keys; the step is one dspark_step call (draft, then schedule and verify)"}
+
+
 def time_w2_cold(torch, run, reps: int = 10, scratch_bytes: int = 512 << 20):
     """The draft call with W2 (and everything else) evicted from the on-chip
     and memory-side caches first: a 512 MB scratch buffer is streamed (read
@@ -375,6 +413,7 @@ def main():
 
     from semi_ar_drafter_amd import (markov_draft, parallel_draft, rnn_draft, schedule, schedule_workspace_bytes,
                                      serve, set_draft_launch, sts_fit, verify)
+    from semi_ar_drafter_amd import step as dspark_step
     from semi_ar_drafter_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -612,6 +651,8 @@ def main():
                               "marginal_us_vs_markov": round(rnn_us - draft_avg * 1e3, 2),
                               "note": "dspark_rnn_draft (per-channel decayed recurrent state) on the same inputs, "
                                       "timed separately from the step"}
+    if not args.no_extras and args.config == 3:
+        result["latency_case"] = time_latency_case(torch, wl, dev, markov_draft, dspark_step)
     if not args.no_sts:
         result["sts_fit"] = time_sts_fit(torch, wl, sts_fit)
     if not args.no_serve:
