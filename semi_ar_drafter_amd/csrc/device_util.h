@@ -98,6 +98,17 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
   return -__builtin_amdgcn_logf(l) * ln2;
 }
 
+// The arg-max of z + G only needs G up to a constant: with L2 = -log2 u
+// (so that -ln u = L2 ln 2), G = -ln(L2) - ln(ln 2), and the score
+// z - ln 2 * log2(L2) is z + G + ln(ln 2), the same shift for every id.  It
+// takes one multiply fewer per id; the drafting kernels rank by it (the
+// unperturbed logit travels with the winner separately).
+__device__ __forceinline__ float gumbel_shifted_from_word(uint32_t w) {
+  const float one_plus = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9u));
+  const float u = one_plus - 0x1.fffffep-1f;
+  return -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(u)) * 0.693147180559945309f;
+}
+
 // 16-byte direct-to-LDS load (gfx950 global_load_lds_dwordx4): lane j of the
 // wave copies 16 bytes from its own global address `src` to lds_base + 16 * j.
 // lds_base must be the same for every lane.  Completion is tracked by the

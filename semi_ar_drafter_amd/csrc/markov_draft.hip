@@ -437,8 +437,8 @@ struct TileWork {
     }
 #pragma unroll
     for (int t = 0; t < NTF; ++t)
-      g[t] = f32x4_t{gumbel_from_word(w[t][0]), gumbel_from_word(w[t][1]), gumbel_from_word(w[t][2]),
-                     gumbel_from_word(w[t][3])};
+      g[t] = f32x4_t{gumbel_shifted_from_word(w[t][0]), gumbel_shifted_from_word(w[t][1]),
+                     gumbel_shifted_from_word(w[t][2]), gumbel_shifted_from_word(w[t][3])};
   }
 
   // g: the whole-tile path's noise of request tile bt (unused otherwise).
@@ -457,7 +457,8 @@ struct TileWork {
       if constexpr (GUMBEL && CHECKED) {
         uint32_t c0 = uint32_t(tile_id0(t)) >> 2, c1 = uint32_t(k), c2 = uint32_t(b), c3 = 0u;
         philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
-        s4 += f32x4_t{gumbel_from_word(c0), gumbel_from_word(c1), gumbel_from_word(c2), gumbel_from_word(c3)};
+        s4 += f32x4_t{gumbel_shifted_from_word(c0), gumbel_shifted_from_word(c1), gumbel_shifted_from_word(c2),
+                      gumbel_shifted_from_word(c3)};
       }
       if constexpr (CHECKED) {   // ids past the vocabulary never win
         const int v0 = tile_id0(t);

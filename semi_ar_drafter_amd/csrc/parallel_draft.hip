@@ -44,14 +44,14 @@ __global__ __launch_bounds__(kPThreads) void parallel_draft_kernel(int gamma, in
   float bs = -INFINITY, bz = 0.f;
   int bi = -1;
   auto noisy = [&](int v0, float* s, const float* z, int n) {
-    // s = z + G for ids v0 .. v0+n-1 (v0 a multiple of 4, n a multiple of 4)
+    // s = z + G + ln(ln 2) for ids v0 .. v0+n-1 (v0 a multiple of 4, n a multiple of 4)
     for (int g = 0; g < n; g += 4) {
       uint32_t c0 = uint32_t(v0 + g) >> 2, c1 = uint32_t(k), c2 = uint32_t(b), c3 = 0u;
       philox4x32_10(c0, c1, c2, c3, seed_lo, seed_hi);
-      s[g + 0] = z[g + 0] + gumbel_from_word(c0);
-      s[g + 1] = z[g + 1] + gumbel_from_word(c1);
-      s[g + 2] = z[g + 2] + gumbel_from_word(c2);
-      s[g + 3] = z[g + 3] + gumbel_from_word(c3);
+      s[g + 0] = z[g + 0] + gumbel_shifted_from_word(c0);
+      s[g + 1] = z[g + 1] + gumbel_shifted_from_word(c1);
+      s[g + 2] = z[g + 2] + gumbel_shifted_from_word(c2);
+      s[g + 3] = z[g + 3] + gumbel_shifted_from_word(c3);
     }
   };
   auto take_chunk = [&](int v0, const float* z) {
