@@ -117,3 +117,13 @@ def test_serve_qwen3_8b_shape():
     the draft is checked on a sample of requests, schedule and verify on all."""
     g = serve_case(wl.WORKLOADS[2], 3, "global", rows=[0, 17, 33, 63])
     assert g["m"].min() > 0
+
+
+@pytest.mark.parametrize("sampling,dtype,r,policy", [("greedy", "bf16", 256, "global"),
+                                                     ("gumbel", "bf16", 256, "global_delayed2"),
+                                                     ("greedy", "f32", 16, "threshold")])
+def test_serve_small_batch(sampling, dtype, r, policy):
+    """Batches of at most 16 requests: the drafting kernels synchronise through
+    the workgroups' winner keys, chained over iterations on one workspace."""
+    cfg = wl.small_config(B=4, gamma=6, V=5000, r=r, d=16, dtype=dtype, sampling=sampling)
+    serve_case(cfg, 5, policy)
