@@ -54,6 +54,7 @@ CASES = [
     (2, 3, 3001, 256, 16, "greedy"),          # guarded kernel
     (8, 4, 65536, 256, 16, "greedy"),
     (16, 3, 65536, 256, 16, "gumbel"),        # the largest such batch: two requests per wave
+    (2, 4, 151936, 256, 16, "gumbel"),        # five slots per wave
 ]
 
 

@@ -78,6 +78,8 @@ CASES = {
     "fused limit, two keys per thread": dict(B=64, gamma=16, V=65536, r=256, d=32, dtype="bf16"),
     "five slots per wave, gumbel": dict(B=17, gamma=16, V=151936, r=256, d=32, dtype="bf16", sampling="gumbel"),
     "above the fused limit": dict(B=65, gamma=16, V=65536, r=256, d=32, dtype="bf16"),
+    "small batch, two requests per wave, gumbel": dict(B=16, gamma=8, V=65536, r=256, d=32, dtype="bf16",
+                                                       sampling="gumbel"),
     "three launches, bf16 r=32": dict(B=10, gamma=3, V=3001, r=32, d=20, dtype="bf16", sampling="gumbel"),
     "three launches, fp32": dict(B=5, gamma=4, V=1030, r=16, d=12, dtype="f32"),
 }
